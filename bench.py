@@ -1,0 +1,247 @@
+"""Benchmark of the DeepSeekMoE layer forward pass on one MI355X.
+
+One step = one call of moe_layer_forward (router, dispatch, routed + shared expert FFNs,
+combine + residual) over the V3-style workload: T=16384 tokens, H=7168, 1 shared + 256 routed
+SwiGLU experts of width 2048, top-8, sigmoid + selection bias, bf16 with fp32 accumulation.
+Inputs are seeded synthetic tensors of that shape (no trained weights), resident in HBM before
+timing starts.  The decode regime (the first 128 tokens of the same inputs) is timed as well.
+
+Prints one JSON line.  Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np
+
+METRIC = "MoE-layer tokens/s and TFLOP/s (% bf16 MFMA peak) at V3-style shape; decode HBM GB/s"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+
+# ---------------------------------------------------------------- algorithmic work counters
+
+def ffn_params(n_experts, H, I, act_swiglu=True):
+    """Weights of n_experts FFNs of width I: SwiGLU has gate, up and down (3 H*I), ReLU two (2 H*I)."""
+    return n_experts * (3 if act_swiglu else 2) * H * I
+
+
+def ffn_flops_per_token(k, H, I, act_swiglu=True):
+    """FLOPs (2 per multiply-add) of k expert FFNs of width I on one token."""
+    return 2 * k * (3 if act_swiglu else 2) * H * I
+
+
+def layer_flops(w, T=None):
+    """Router GEMM plus the FFNs of the selected and shared experts (no padding, no elementwise)."""
+    T = w.T if T is None else T
+    sw = w.act == 1
+    return 2 * T * w.H * w.N_r + T * ffn_flops_per_token(w.K_r + w.Ks, w.H, w.I, sw)
+
+
+def routed_up_flops(w, T=None):
+    """FLOPs of the routed gate/up GEMM (the dominant kernel): T*K_r rows x (2I or I) x H."""
+    T = w.T if T is None else T
+    n1 = 2 * w.I if w.act == 1 else w.I
+    return 2 * T * w.K_r * n1 * w.H
+
+
+def decode_bytes(w, n_touched, T=None):
+    """HBM bytes a decode step must move at least: weights of the touched routed experts and of the
+    shared experts, the centroids, the tokens in and the outputs out (bf16)."""
+    T = w.T if T is None else T
+    e = 2 if w.dtype == 1 else 4
+    per_expert = ffn_params(1, w.H, w.I, w.act == 1) * e
+    return n_touched * per_expert + w.Ks * per_expert + w.N_r * w.H * e + 2 * T * w.H * e
+
+
+# ---------------------------------------------------------------- timing helpers
+
+def _upload(inp):
+    import torch
+    out = {}
+    for k, v in inp.items():
+        if v is None:
+            out[k] = None
+            continue
+        t = torch.from_numpy(np.ascontiguousarray(v))
+        if v.dtype == np.uint16:
+            t = t.view(torch.bfloat16)
+        out[k] = t.cuda()
+    return out
+
+
+def _time_steps(fn, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(s)
+    for _ in range(steps):
+        fn()
+    b.record(s)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
+def _kernel_times(fn, steps):
+    """Average duration per launch of each kernel class, from HIP events the library records
+    on the launch stream around every kernel."""
+    import torch
+    import fine_grained_shared_amd as moe
+    torch.cuda.synchronize()
+    moe.moe_profile_enable(True)
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    moe.moe_profile_enable(False)
+    res = {}
+    for k, name in enumerate(moe.PROF_NAMES):
+        n, ms = moe.moe_profile_query(k)
+        if n:
+            res[name] = {"launches_per_step": n / steps, "ms_per_step": ms / steps}
+    return res
+
+
+def cpu_baseline(w, inp, budget_s=15.0):
+    """The fp64 oracle on the host cores, on a bounded sample of the workload's tokens."""
+    import oracle
+    s = oracle.shape_of(w)
+    probe = np.arange(0, w.T, max(1, w.T // 8))[:8].astype(np.int64)
+    t0 = time.time()
+    oracle.layer(s, inp, tokens=probe)
+    per_tok = max((time.time() - t0) / len(probe), 1e-6)
+    n = int(min(max(budget_s / per_tok, 8), w.T))
+    toks = np.linspace(0, w.T - 1, n).astype(np.int64)
+    t0 = time.time()
+    oracle.layer(s, inp, tokens=toks)
+    dt = time.time() - t0
+    return {"value": round(n / dt, 3), "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": "%d of %d tokens (evenly strided) of the same layer, full forward in fp64, %.1f s" % (
+                n, w.T, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="c3p")
+    ap.add_argument("--decode-tokens", type=int, default=128)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the layer runs data-parallel over tokens with replicated "
+              "weights, so no exchange is needed and N>1 is not measured here (use --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import fine_grained_shared_amd as moe
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    moe.load()
+    w = synth.WORKLOADS[args.workload]
+    t0 = time.time()
+    inp = synth.make_inputs(w)
+    gen_s = time.time() - t0
+    d = _upload(inp)
+    torch.cuda.synchronize()
+    print("[bench] inputs generated in %.1f s and uploaded" % gen_s, file=sys.stderr, flush=True)
+
+    # plain 1 GiB device copy: reference point for the HBM byte counters of a profiled run
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    del src, dst
+
+    shape = moe.make_shape(w.T, w.H, w.N_r, w.K_r, w.Ks, w.I, w.gating, w.act, w.dtype)
+    ws = moe.workspace(shape)
+    out = torch.empty((w.T, w.H), dtype=moe.torch_dtype(shape), device="cuda")
+    idx = torch.empty((w.T, w.K_r), dtype=torch.int32, device="cuda")
+    wts = torch.empty((w.T, w.K_r), dtype=torch.float32, device="cuda")
+
+    def step():
+        moe.moe_layer_forward(shape, d["u"], d["centroids"], d["bias"], d["w1"], d["b1"], d["w2"], d["w1_sh"],
+                              d["b1_sh"], d["w2_sh"], 0, out, idx, wts, ws)
+
+    ms = _time_steps(step, args.steps, args.warmup)
+    print("[bench] prefill %.3f ms/step" % ms, file=sys.stderr, flush=True)
+    kt = _kernel_times(step, max(2, min(args.steps, 10)))
+    flops = layer_flops(w)
+    up = kt.get("ffn_up", {"ms_per_step": float("nan"), "launches_per_step": 1})
+    up_ms = up["ms_per_step"] / up["launches_per_step"]
+    up_tflops = routed_up_flops(w) / (up_ms * 1e-3) / 1e12
+    counts = np.bincount(idx.cpu().numpy().reshape(-1), minlength=w.N_r)
+
+    result = {
+        "metric": METRIC,
+        "value": round(w.T / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) tokens, N(0,1/fan_in) weights, N(0,1/H) centroids, bias N(0,0.01))",
+        "config": {"workload": w.desc, "T": w.T, "H": w.H, "N_r": w.N_r, "K_r": w.K_r, "Ks": w.Ks, "I": w.I,
+                   "gating": "sigmoid+selection bias, normalised over selected",
+                   "act": "SwiGLU", "parallelism": "single GPU"},
+        "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+        "pct_bf16_peak": round(100 * flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"kernel": "routed expert gate/up grouped GEMM + SwiGLU (k_gemm_bf16<UP_SWIGLU>)",
+                     "bound": "mfma", "achieved": round(up_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(up_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "avg_launch_ms": round(up_ms, 4),
+                     "algorithmic_flops_per_launch": routed_up_flops(w)},
+        "kernels_ms_per_step": {k: round(v["ms_per_step"], 4) for k, v in kt.items()},
+        "load": {"touched": int((counts > 0).sum()), "empty": int((counts == 0).sum()),
+                 "max_over_mean": round(float(counts.max() / counts.mean()), 2)},
+    }
+
+    if not args.no_decode:
+        Td = args.decode_tokens
+        wd = w.with_(T=Td)
+        sd = moe.make_shape(Td, w.H, w.N_r, w.K_r, w.Ks, w.I, w.gating, w.act, w.dtype)
+        wsd = moe.workspace(sd)
+        ud = d["u"][:Td].contiguous()
+        outd = torch.empty((Td, w.H), dtype=moe.torch_dtype(sd), device="cuda")
+        idxd = torch.empty((Td, w.K_r), dtype=torch.int32, device="cuda")
+        wtd = torch.empty((Td, w.K_r), dtype=torch.float32, device="cuda")
+
+        def dstep():
+            moe.moe_layer_forward(sd, ud, d["centroids"], d["bias"], d["w1"], d["b1"], d["w2"], d["w1_sh"],
+                                  d["b1_sh"], d["w2_sh"], 0, outd, idxd, wtd, wsd)
+
+        dms = _time_steps(dstep, max(args.steps, 10), args.warmup)
+        dkt = _kernel_times(dstep, 10)
+        touched = int(np.unique(idxd.cpu().numpy()).size)
+        nbytes = decode_bytes(wd, touched)
+        gbs = nbytes / (dms * 1e-3) / 1e9
+        result["decode"] = {"T": Td, "ms_per_step": round(dms, 4), "tokens_per_s": round(Td / (dms * 1e-3), 1),
+                            "touched_experts": touched, "algorithmic_bytes": nbytes, "GB_per_s": round(gbs, 1),
+                            "pct_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
+                            "kernels_ms_per_step": {k: round(v["ms_per_step"], 4) for k, v in dkt.items()}}
+        print("[bench] decode %.3f ms/step, %.0f GB/s" % (dms, gbs), file=sys.stderr, flush=True)
+
+    if not args.no_cpu:
+        print("[bench] timing the fp64 oracle on the host cores", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(w, inp)
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,430 @@
+// C ABI of libmoe (declared in include/moe.h): argument checks, workspace carving, launches.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+#include <string.h>
+
+#include <vector>
+
+#include "../../include/moe.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+// ---------------------------------------------------------------- kernel timing
+struct Prof {
+    bool on = false;
+    std::vector<hipEvent_t> ev;  // pairs
+    std::vector<int> cls;
+    size_t used = 0;
+};
+Prof g_prof;
+constexpr size_t kProfPairs = 8192;
+
+struct ProfScope {
+    bool rec = false;
+    hipEvent_t b = nullptr;
+    hipStream_t s;
+    ProfScope(int c, hipStream_t st) : s(st) {
+        if (!g_prof.on || g_prof.used >= kProfPairs) return;
+        const size_t i = g_prof.used++;
+        g_prof.cls[i] = c;
+        rec = hipEventRecord(g_prof.ev[2 * i], s) == hipSuccess;
+        b = g_prof.ev[2 * i + 1];
+    }
+    ~ProfScope() {
+        if (rec) (void)hipEventRecord(b, s);
+    }
+};
+
+int hip_fail(hipError_t e) {
+    g_last_hip_error = (int)e;
+    return MOE_ERR_HIP;
+}
+#define MOE_TRY(cls, stream, expr)                     \
+    do {                                               \
+        hipError_t e_;                                 \
+        {                                              \
+            ProfScope ps_(cls, stream);                \
+            e_ = (expr);                               \
+        }                                              \
+        if (e_ != hipSuccess) return hip_fail(e_);     \
+    } while (0)
+
+// ---------------------------------------------------------------- validation
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_shape(const moe_shape* s) {
+    if (!s) return MOE_ERR_INVALID_ARG;
+    if (s->T < 0 || s->H <= 0 || s->N_r < 0 || s->K_r < 0 || s->Ks < 0 || s->I <= 0) return MOE_ERR_INVALID_ARG;
+    if (s->K_r > s->N_r) return MOE_ERR_INVALID_ARG;
+    if (s->gating < 0 || s->gating > 2 || s->act < 0 || s->act > 1 || s->dtype < 0 || s->dtype > 1)
+        return MOE_ERR_INVALID_ARG;
+    if (s->H % 64 || s->I % 64) return MOE_ERR_INVALID_ARG;
+    if (s->n_group < 0 || s->mask_top_r < 0 || s->mask_top_r + s->K_r > s->N_r) return MOE_ERR_INVALID_ARG;
+    if (s->n_group > 0) {
+        if (s->N_r % s->n_group || s->topk_group <= 0 || s->topk_group > s->n_group) return MOE_ERR_INVALID_ARG;
+        if ((long long)s->topk_group * (s->N_r / s->n_group) < s->K_r) return MOE_ERR_INVALID_ARG;
+        if (s->mask_top_r) return MOE_ERR_INVALID_ARG;
+    }
+    if (s->N_r > 1024 || s->K_r > 64 || s->n_group > 64) return MOE_ERR_UNSUPPORTED;
+    if ((long long)s->T * (s->K_r > 0 ? s->K_r : 1) > 0x7FFFFFFFLL) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+size_t esz(const moe_shape* s) { return s->dtype == MOE_F32 ? 4 : 2; }
+
+// Workspace regions (byte offsets, each 256-byte aligned).
+struct Layout {
+    size_t logits, topk_idx, topk_w, offsets, row_token, pair_row, chunks, tiles, act, y_perm, act_sh, y_sh, total;
+};
+
+Layout layout_of(const moe_shape* s) {
+    Layout L{};
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = o;
+        o += (bytes + 255) / 256 * 256;
+        return at;
+    };
+    const size_t T = (size_t)s->T, R = (size_t)s->T * s->K_r, E = esz(s);
+    const size_t nchunk = (T + moe::kChunk - 1) / moe::kChunk;
+    L.logits = take(T * s->N_r * 4);
+    L.topk_idx = take(R * 4);
+    L.topk_w = take(R * 4);
+    L.offsets = take(((size_t)s->N_r + 1) * 4);
+    L.row_token = take(R * 4);
+    L.pair_row = take(R * 4);
+    L.chunks = take(nchunk * s->N_r * 4);
+    L.tiles = take(((size_t)s->N_r + 1) * 4);
+    L.act = take(R * s->I * E);
+    L.y_perm = take(R * s->H * E);
+    L.act_sh = take(T * s->Ks * s->I * E);
+    L.y_sh = take(T * s->H * E);
+    L.total = o;
+    return L;
+}
+
+template <typename P>
+P* at(void* ws, size_t off) {
+    return reinterpret_cast<P*>(static_cast<char*>(ws) + off);
+}
+
+int check_ws(const moe_shape* s, void* ws, size_t ws_bytes) {
+    const Layout L = layout_of(s);
+    if (L.total > 0 && (!ws || ws_bytes < L.total || !aligned16(ws))) return MOE_ERR_WORKSPACE;
+    return MOE_OK;
+}
+
+// ---------------------------------------------------------------- steps
+int do_route(const moe_shape* s, const void* u, const void* e, const float* bias, int32_t* idx, float* w,
+             float* logits, hipStream_t st) {
+    if (s->T == 0 || s->K_r == 0) return MOE_OK;
+    MOE_TRY(MOE_PROF_ROUTER, st, moe::launch_logits(s->dtype, u, e, logits, s->T, s->H, s->N_r, st));
+    moe::SelectArgs a{logits, bias, s->T, s->N_r, s->K_r, s->gating, s->n_group, s->topk_group, s->mask_top_r,
+                      idx, w};
+    MOE_TRY(MOE_PROF_ROUTER, st, moe::launch_select(a, st));
+    return MOE_OK;
+}
+
+int do_dispatch(const moe_shape* s, const int32_t* idx, int32_t* offsets, int32_t* row_token, int32_t* pair_row,
+                int32_t* chunks, hipStream_t st) {
+    const int nchunk = (s->T + moe::kChunk - 1) / moe::kChunk;
+    MOE_TRY(MOE_PROF_DISPATCH, st, moe::launch_count(idx, s->T, s->K_r, s->N_r, chunks, st));
+    MOE_TRY(MOE_PROF_DISPATCH, st, moe::launch_scan(chunks, s->K_r > 0 ? nchunk : 0, s->N_r, offsets, st));
+    MOE_TRY(MOE_PROF_DISPATCH, st, moe::launch_scatter(idx, s->T, s->K_r, s->N_r, chunks, row_token, pair_row, st));
+    return MOE_OK;
+}
+
+int do_expert_ffn(const moe_shape* s, const void* x, const int32_t* row_token, const int32_t* offsets,
+                  const void* w1, const float* b1, const void* w2, void* y, int32_t* tiles, void* act,
+                  hipStream_t st) {
+    const long long R = (long long)s->T * s->K_r;
+    if (R == 0 || s->N_r == 0) return MOE_OK;
+    const int n1 = s->act == MOE_ACT_SWIGLU ? 2 * s->I : s->I;
+    if (s->dtype == MOE_BF16)
+        MOE_TRY(MOE_PROF_OTHER, st, moe::launch_tile_plan(offsets, s->N_r, moe::gemm_bm(s->dtype), tiles, st));
+    moe::GemmParams up{};
+    up.A = x;
+    up.lda = s->H;
+    up.a_rows = row_token;
+    up.a_nrows = row_token ? s->T : R;
+    up.B = w1;
+    up.sB_group = (long long)n1 * s->H;
+    up.ldb = s->H;
+    up.K = s->H;
+    up.Kseg = s->H;
+    up.sB_seg = 0;
+    up.N = s->I;
+    up.up_off = s->I;
+    up.offsets = offsets;
+    up.tiles = tiles;
+    up.G = s->N_r;
+    up.max_rows = (int)R;
+    up.C = act;
+    up.ldc = s->I;
+    up.bias = b1;
+    up.sbias_group = s->I;
+    const int up_mode = s->act == MOE_ACT_SWIGLU ? moe::GM_UP_SWIGLU : moe::GM_UP_RELU;
+    MOE_TRY(MOE_PROF_FFN_UP, st, moe::launch_gemm(s->dtype, up_mode, up, st));
+    moe::GemmParams dn{};
+    dn.A = act;
+    dn.lda = s->I;
+    dn.a_rows = nullptr;
+    dn.a_nrows = R;
+    dn.B = w2;
+    dn.sB_group = (long long)s->H * s->I;
+    dn.ldb = s->I;
+    dn.K = s->I;
+    dn.Kseg = s->I;
+    dn.N = s->H;
+    dn.offsets = offsets;
+    dn.tiles = tiles;
+    dn.G = s->N_r;
+    dn.max_rows = (int)R;
+    dn.C = y;
+    dn.ldc = s->H;
+    MOE_TRY(MOE_PROF_FFN_DOWN, st, moe::launch_gemm(s->dtype, moe::GM_DOWN, dn, st));
+    return MOE_OK;
+}
+
+int do_shared_ffn(const moe_shape* s, const void* x, const void* w1, const float* b1, const void* w2, void* y,
+                  void* act, hipStream_t st) {
+    if (s->T == 0 || s->Ks == 0) return MOE_OK;
+    const int n1 = s->act == MOE_ACT_SWIGLU ? 2 * s->I : s->I;
+    moe::GemmParams up{};
+    up.A = x;
+    up.lda = s->H;
+    up.a_nrows = s->T;
+    up.B = w1;
+    up.sB_group = (long long)n1 * s->H;
+    up.ldb = s->H;
+    up.K = s->H;
+    up.Kseg = s->H;
+    up.N = s->I;
+    up.up_off = s->I;
+    up.M_dense = s->T;
+    up.G = s->Ks;
+    up.max_rows = s->T;
+    up.C = act;
+    up.ldc = (long long)s->Ks * s->I;
+    up.sC_group = s->I;
+    up.bias = b1;
+    up.sbias_group = s->I;
+    const int up_mode = s->act == MOE_ACT_SWIGLU ? moe::GM_UP_SWIGLU : moe::GM_UP_RELU;
+    MOE_TRY(MOE_PROF_SHARED_UP, st, moe::launch_gemm(s->dtype, up_mode, up, st));
+    // down: one GEMM whose reduction runs over the Ks intermediates side by side
+    moe::GemmParams dn{};
+    dn.A = act;
+    dn.lda = (long long)s->Ks * s->I;
+    dn.a_nrows = s->T;
+    dn.B = w2;
+    dn.sB_group = 0;
+    dn.ldb = s->I;
+    dn.K = s->Ks * s->I;
+    dn.Kseg = s->I;
+    dn.sB_seg = (long long)s->H * s->I;
+    dn.N = s->H;
+    dn.M_dense = s->T;
+    dn.G = 1;
+    dn.max_rows = s->T;
+    dn.C = y;
+    dn.ldc = s->H;
+    MOE_TRY(MOE_PROF_SHARED_DOWN, st, moe::launch_gemm(s->dtype, moe::GM_DOWN, dn, st));
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_workspace_size(const moe_shape* shape, size_t* bytes) {
+    const int rc = check_shape(shape);
+    if (rc != MOE_OK) return rc;
+    if (!bytes) return MOE_ERR_INVALID_ARG;
+    *bytes = layout_of(shape).total;
+    return MOE_OK;
+}
+
+int moe_route(const moe_shape* s, const void* u, const void* centroids, const float* bias, int32_t* topk_idx,
+              float* topk_w, void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_shape(s);
+    if (rc != MOE_OK) return rc;
+    if (bias && s->gating != MOE_GATE_SIGMOID_BIAS_NORM) return MOE_ERR_INVALID_ARG;
+    if (s->T == 0 || s->K_r == 0) return MOE_OK;
+    if (!u || !centroids || !topk_idx || !topk_w || !aligned16(u) || !aligned16(centroids))
+        return MOE_ERR_INVALID_ARG;
+    if ((rc = check_ws(s, ws, ws_bytes)) != MOE_OK) return rc;
+    const Layout L = layout_of(s);
+    return do_route(s, u, centroids, bias, topk_idx, topk_w, at<float>(ws, L.logits), (hipStream_t)stream);
+}
+
+int moe_dispatch(const moe_shape* s, const int32_t* topk_idx, int32_t* offsets, int32_t* row_token,
+                 int32_t* pair_row, const void* u, void* x_perm, void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_shape(s);
+    if (rc != MOE_OK) return rc;
+    if (!offsets) return MOE_ERR_INVALID_ARG;
+    const long long R = (long long)s->T * s->K_r;
+    if (R > 0 && (!topk_idx || !row_token || !pair_row)) return MOE_ERR_INVALID_ARG;
+    if ((u == nullptr) != (x_perm == nullptr)) return MOE_ERR_INVALID_ARG;
+    if (x_perm && (!aligned16(u) || !aligned16(x_perm))) return MOE_ERR_INVALID_ARG;
+    if ((rc = check_ws(s, ws, ws_bytes)) != MOE_OK) return rc;
+    const Layout L = layout_of(s);
+    hipStream_t st = (hipStream_t)stream;
+    rc = do_dispatch(s, topk_idx, offsets, row_token, pair_row, at<int32_t>(ws, L.chunks), st);
+    if (rc != MOE_OK) return rc;
+    if (x_perm) MOE_TRY(MOE_PROF_DISPATCH, st, moe::launch_gather(s->dtype, u, row_token, (int)R, s->H, x_perm, st));
+    return MOE_OK;
+}
+
+int moe_expert_ffn(const moe_shape* s, const void* x, const int32_t* row_token, const int32_t* offsets,
+                   const void* w1, const float* b1, const void* w2, void* y, void* ws, size_t ws_bytes,
+                   void* stream) {
+    int rc = check_shape(s);
+    if (rc != MOE_OK) return rc;
+    const long long R = (long long)s->T * s->K_r;
+    if (R == 0) return MOE_OK;
+    if (!x || !offsets || !w1 || !w2 || !y) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(w1) || !aligned16(w2) || !aligned16(y)) return MOE_ERR_INVALID_ARG;
+    if (b1 && s->act != MOE_ACT_RELU_BIAS) return MOE_ERR_INVALID_ARG;
+    if ((rc = check_ws(s, ws, ws_bytes)) != MOE_OK) return rc;
+    const Layout L = layout_of(s);
+    return do_expert_ffn(s, x, row_token, offsets, w1, b1, w2, y, at<int32_t>(ws, L.tiles), at<void>(ws, L.act),
+                         (hipStream_t)stream);
+}
+
+int moe_shared_ffn(const moe_shape* s, const void* x, const void* w1_sh, const float* b1_sh, const void* w2_sh,
+                   void* y, void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_shape(s);
+    if (rc != MOE_OK) return rc;
+    if (s->T == 0 || s->Ks == 0) return MOE_OK;
+    if (!x || !w1_sh || !w2_sh || !y) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(w1_sh) || !aligned16(w2_sh) || !aligned16(y)) return MOE_ERR_INVALID_ARG;
+    if (b1_sh && s->act != MOE_ACT_RELU_BIAS) return MOE_ERR_INVALID_ARG;
+    if ((rc = check_ws(s, ws, ws_bytes)) != MOE_OK) return rc;
+    const Layout L = layout_of(s);
+    return do_shared_ffn(s, x, w1_sh, b1_sh, w2_sh, y, at<void>(ws, L.act_sh), (hipStream_t)stream);
+}
+
+int moe_combine(const moe_shape* s, const void* residual, const void* y_shared, const void* y_perm,
+                const int32_t* pair_row, const float* topk_w, void* out, void* stream) {
+    int rc = check_shape(s);
+    if (rc != MOE_OK) return rc;
+    if (s->T == 0) return MOE_OK;
+    if (!out || !aligned16(out)) return MOE_ERR_INVALID_ARG;
+    if (s->K_r > 0 && (!y_perm || !pair_row || !topk_w || !aligned16(y_perm))) return MOE_ERR_INVALID_ARG;
+    if ((residual && !aligned16(residual)) || (y_shared && !aligned16(y_shared))) return MOE_ERR_INVALID_ARG;
+    hipStream_t st = (hipStream_t)stream;
+    MOE_TRY(MOE_PROF_COMBINE, st, moe::launch_combine(s->dtype, residual, y_shared, y_perm, pair_row, topk_w, out,
+                                                      s->T, s->H, s->K_r, st));
+    return MOE_OK;
+}
+
+int moe_layer_forward(const moe_shape* s, const void* u, const void* centroids, const float* bias, const void* w1,
+                      const float* b1, const void* w2, const void* w1_sh, const float* b1_sh, const void* w2_sh,
+                      int32_t flags, void* out, int32_t* topk_idx_out, float* topk_w_out, void* ws, size_t ws_bytes,
+                      void* stream) {
+    int rc = check_shape(s);
+    if (rc != MOE_OK) return rc;
+    if (flags & ~MOE_FLAG_NO_RESIDUAL) return MOE_ERR_INVALID_ARG;
+    if (bias && s->gating != MOE_GATE_SIGMOID_BIAS_NORM) return MOE_ERR_INVALID_ARG;
+    if ((b1 || b1_sh) && s->act != MOE_ACT_RELU_BIAS) return MOE_ERR_INVALID_ARG;
+    if (s->T == 0) return MOE_OK;
+    if (!u || !out || !aligned16(u) || !aligned16(out)) return MOE_ERR_INVALID_ARG;
+    if (s->K_r > 0 && (!centroids || !w1 || !w2 || !aligned16(centroids) || !aligned16(w1) || !aligned16(w2)))
+        return MOE_ERR_INVALID_ARG;
+    if (s->Ks > 0 && (!w1_sh || !w2_sh || !aligned16(w1_sh) || !aligned16(w2_sh))) return MOE_ERR_INVALID_ARG;
+    if ((rc = check_ws(s, ws, ws_bytes)) != MOE_OK) return rc;
+    const Layout L = layout_of(s);
+    hipStream_t st = (hipStream_t)stream;
+    int32_t* idx = topk_idx_out ? topk_idx_out : at<int32_t>(ws, L.topk_idx);
+    float* wts = topk_w_out ? topk_w_out : at<float>(ws, L.topk_w);
+    int32_t* offsets = at<int32_t>(ws, L.offsets);
+    int32_t* pair_row = at<int32_t>(ws, L.pair_row);
+    void* y_perm = at<void>(ws, L.y_perm);
+    void* y_sh = at<void>(ws, L.y_sh);
+    if (s->K_r > 0) {
+        if ((rc = do_route(s, u, centroids, bias, idx, wts, at<float>(ws, L.logits), st)) != MOE_OK) return rc;
+        if ((rc = do_dispatch(s, idx, offsets, at<int32_t>(ws, L.row_token), pair_row, at<int32_t>(ws, L.chunks),
+                              st)) != MOE_OK)
+            return rc;
+        if ((rc = do_expert_ffn(s, u, at<int32_t>(ws, L.row_token), offsets, w1, b1, w2, y_perm,
+                                at<int32_t>(ws, L.tiles), at<void>(ws, L.act), st)) != MOE_OK)
+            return rc;
+    }
+    if (s->Ks > 0) {
+        if ((rc = do_shared_ffn(s, u, w1_sh, b1_sh, w2_sh, y_sh, at<void>(ws, L.act_sh), st)) != MOE_OK) return rc;
+    }
+    MOE_TRY(MOE_PROF_COMBINE, st,
+            moe::launch_combine(s->dtype, (flags & MOE_FLAG_NO_RESIDUAL) ? nullptr : u, s->Ks > 0 ? y_sh : nullptr,
+                                y_perm, pair_row, wts, out, s->T, s->H, s->K_r, st));
+    return MOE_OK;
+}
+
+int moe_bias_update(const moe_shape* s, const int32_t* offsets, float gamma, float* bias, int32_t* counts,
+                    void* stream) {
+    int rc = check_shape(s);
+    if (rc != MOE_OK) return rc;
+    if (s->N_r == 0) return MOE_OK;
+    if (!offsets || !bias) return MOE_ERR_INVALID_ARG;
+    hipStream_t st = (hipStream_t)stream;
+    MOE_TRY(MOE_PROF_OTHER, st, moe::launch_bias_update(offsets, s->N_r, s->T, s->K_r, gamma, bias, counts, st));
+    return MOE_OK;
+}
+
+const char* moe_status_string(int status) {
+    switch (status) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_INVALID_ARG: return "invalid argument";
+        case MOE_ERR_UNSUPPORTED: return "unsupported shape";
+        case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+        case MOE_ERR_HIP: return "HIP error";
+        default: return "unknown status";
+    }
+}
+
+int moe_last_hip_error(void) { return g_last_hip_error; }
+
+int moe_profile_enable(int32_t on) {
+    if (on) {
+        if (g_prof.ev.empty()) {
+            g_prof.ev.resize(2 * kProfPairs);
+            g_prof.cls.resize(kProfPairs);
+            for (auto& e : g_prof.ev) {
+                const hipError_t r = hipEventCreate(&e);
+                if (r != hipSuccess) {
+                    g_prof.ev.clear();
+                    return hip_fail(r);
+                }
+            }
+        }
+        g_prof.used = 0;
+        g_prof.on = true;
+    } else {
+        g_prof.on = false;
+    }
+    return MOE_OK;
+}
+
+int moe_profile_query(int32_t kernel, int64_t* launches, double* total_ms) {
+    if (kernel < 0 || kernel >= MOE_PROF_COUNT || !launches || !total_ms) return MOE_ERR_INVALID_ARG;
+    int64_t n = 0;
+    double ms = 0.0;
+    for (size_t i = 0; i < g_prof.used; ++i) {
+        if (g_prof.cls[i] != kernel) continue;
+        const hipError_t r = hipEventSynchronize(g_prof.ev[2 * i + 1]);
+        if (r != hipSuccess) return hip_fail(r);
+        float t = 0.f;
+        const hipError_t r2 = hipEventElapsedTime(&t, g_prof.ev[2 * i], g_prof.ev[2 * i + 1]);
+        if (r2 != hipSuccess) return hip_fail(r2);
+        ++n;
+        ms += t;
+    }
+    *launches = n;
+    *total_ms = ms;
+    return MOE_OK;
+}
+
+}  // extern "C"

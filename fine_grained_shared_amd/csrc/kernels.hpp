@@ -1,0 +1,73 @@
+// Host-side launchers of the libmoe kernels (internal; the public ABI is include/moe.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ---------------------------------------------------------------- router
+// logits [T, N] fp32 = u [T, H] . centroids [N, H]^T
+hipError_t launch_logits(int dtype, const void* u, const void* e, float* logits, int T, int H, int N,
+                         hipStream_t s);
+// per-token scores, selection and gate weights from the logits
+struct SelectArgs {
+    const float* logits;
+    const float* bias;
+    int T, N, K;
+    int gating;
+    int n_group, topk_group, mask_r;
+    int32_t* topk_idx;
+    float* topk_w;
+};
+hipError_t launch_select(const SelectArgs& a, hipStream_t s);
+
+// ---------------------------------------------------------------- dispatch
+constexpr int kChunk = 256;  // tokens per dispatch workgroup
+hipError_t launch_count(const int32_t* idx, int T, int K, int N, int32_t* chunk_counts, hipStream_t s);
+hipError_t launch_scan(int32_t* chunk_counts, int nchunk, int N, int32_t* offsets, hipStream_t s);
+hipError_t launch_scatter(const int32_t* idx, int T, int K, int N, const int32_t* chunk_base,
+                          int32_t* row_token, int32_t* pair_row, hipStream_t s);
+hipError_t launch_gather(int dtype, const void* u, const int32_t* row_token, int R, int H, void* x_perm,
+                         hipStream_t s);
+
+// ---------------------------------------------------------------- expert FFN (grouped GEMM)
+enum { GM_UP_SWIGLU = 0, GM_UP_RELU = 1, GM_DOWN = 2 };
+
+struct GemmParams {
+    const void* A;            // activation rows
+    long long lda;            // elements per A row
+    const int32_t* a_rows;    // row-space row -> A row (NULL: identity)
+    long long a_nrows;        // rows of A (gathered indices are clamped into range)
+    const void* B;            // weight bank base
+    long long sB_group;       // elements between groups in the bank
+    long long ldb;            // elements per weight row
+    int K;                    // reduction length
+    int Kseg;                 // reduction segment length; segment q reads B + q * sB_seg
+    long long sB_seg;
+    int N;                    // output columns
+    int up_off;               // SwiGLU: first up row inside a group's w1 (= I)
+    const int32_t* offsets;   // grouped mode: [G+1] row-space segments (NULL: dense mode)
+    const int32_t* tiles;     // grouped mode: [G+1] prefix of m-tiles per group
+    int M_dense;              // dense mode: every group covers rows [0, M_dense)
+    int G;
+    int max_rows;             // upper bound of the row space (grid sizing)
+    void* C;                  // output
+    long long ldc;
+    long long sC_group;       // dense mode: column offset of group g in C is g * sC_group
+    const float* bias;        // ReLU bias [G, N] (NULL = 0)
+    long long sbias_group;
+};
+// m-tile prefix of the groups defined by offsets (grouped mode), for tiles of bm rows
+hipError_t launch_tile_plan(const int32_t* offsets, int G, int bm, int32_t* tiles, hipStream_t s);
+int gemm_bm(int dtype);
+hipError_t launch_gemm(int dtype, int mode, const GemmParams& p, hipStream_t s);
+
+// ---------------------------------------------------------------- combine, controller
+hipError_t launch_combine(int dtype, const void* residual, const void* y_shared, const void* y_perm,
+                          const int32_t* pair_row, const float* topk_w, void* out, int T, int H, int K,
+                          hipStream_t s);
+hipError_t launch_bias_update(const int32_t* offsets, int N, long long T, int K, float gamma, float* bias,
+                              int32_t* counts, hipStream_t s);
+
+}  // namespace moe

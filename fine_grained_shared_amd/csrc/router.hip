@@ -1,0 +1,236 @@
+// Router: logits, scores, top-k selection and gate weights.
+//
+// llm-infra-atlas "02 Fine-grained MoE", section 2.1 (DeepSeekMoE Eq. 7-8): l = u_t . e_i,
+// s = softmax(l), g = s on the top-K set.  Section 3.1 (DeepSeek-V3 Eq. 12-15): s = sigmoid(l),
+// g = s / sum of the selected s.  ibossgateway chapter 7, section 7.4: the ranking uses
+// s + b_i, the weights the raw s.  tomabc explainer: the masked softmax gate.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+// ---------------------------------------------------------------- logits, bf16 (MFMA)
+// Tile: TB*16 tokens x 64 experts per workgroup.  Wave w owns experts [e0 + 16 w, +16) and all
+// TB token blocks; v_mfma_f32_16x16x32_bf16 with both operands read straight from global
+// memory as 16-byte rows (u and the centroids are both K-contiguous).
+template <int TB>
+__global__ __launch_bounds__(256) void k_logits_bf16(const uint16_t* __restrict__ u,
+                                                     const uint16_t* __restrict__ e,
+                                                     float* __restrict__ logits, int T, int H, int N) {
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    const int t0 = blockIdx.x * (TB * 16);
+    const int e0 = blockIdx.y * 64 + w * 16;
+    if (e0 >= N) return;
+    const int r = lane & 15;
+    const int kq = (lane >> 4) * 8;
+    const uint16_t* ap[TB];
+#pragma unroll
+    for (int b = 0; b < TB; ++b) {
+        int t = min(t0 + b * 16 + r, T - 1);
+        ap[b] = u + (size_t)t * H + kq;
+    }
+    const int ex = min(e0 + r, N - 1);
+    const uint16_t* bp = e + (size_t)ex * H + kq;
+    f32x4 acc[TB];
+#pragma unroll
+    for (int b = 0; b < TB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < H; k += 32) {
+        uint4 bv = *reinterpret_cast<const uint4*>(bp + k);
+#pragma unroll
+        for (int b = 0; b < TB; ++b) {
+            uint4 av = *reinterpret_cast<const uint4*>(ap[b] + k);
+            acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
+                                                             __builtin_bit_cast(bf16x8, bv), acc[b], 0, 0, 0);
+        }
+    }
+    // D[i][j]: j = lane % 16 (expert), i = 4 * (lane / 16) + q (token)
+    const int col = e0 + r;
+    if (col < N) {
+#pragma unroll
+        for (int b = 0; b < TB; ++b)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                int t = t0 + b * 16 + (lane >> 4) * 4 + q;
+                if (t < T) logits[(size_t)t * N + col] = acc[b][q];
+            }
+    }
+}
+
+// ---------------------------------------------------------------- logits, fp32 (VALU)
+__global__ __launch_bounds__(256) void k_logits_f32(const float* __restrict__ u, const float* __restrict__ e,
+                                                    float* __restrict__ logits, int T, int H, int N) {
+    const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (long long)T * N) return;
+    const int t = (int)(idx / N), i = (int)(idx % N);
+    const float* a = u + (size_t)t * H;
+    const float* b = e + (size_t)i * H;
+    float acc = 0.f;
+    for (int h = 0; h < H; ++h) acc = fmaf(a[h], b[h], acc);
+    logits[idx] = acc;
+}
+
+hipError_t launch_logits(int dtype, const void* u, const void* e, float* logits, int T, int H, int N,
+                         hipStream_t s) {
+    if (T == 0 || N == 0) return hipSuccess;
+    if (dtype == 0) {
+        long long n = (long long)T * N;
+        hipLaunchKernelGGL(k_logits_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, (const float*)u,
+                           (const float*)e, logits, T, H, N);
+    } else if (T >= 2048) {
+        dim3 grid((T + 63) / 64, (N + 63) / 64);
+        hipLaunchKernelGGL(k_logits_bf16<4>, grid, dim3(256), 0, s, (const uint16_t*)u, (const uint16_t*)e,
+                           logits, T, H, N);
+    } else {
+        dim3 grid((T + 15) / 16, (N + 63) / 64);
+        hipLaunchKernelGGL(k_logits_bf16<1>, grid, dim3(256), 0, s, (const uint16_t*)u, (const uint16_t*)e,
+                           logits, T, H, N);
+    }
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- selection (one wavefront per token)
+// Keys are packed as (order-preserving key bits << 32) | (~index) so that one 64-bit max picks
+// the largest key and, among equal keys, the lower expert index.
+__device__ __forceinline__ uint32_t order_bits(float f) {
+    uint32_t b = __float_as_uint(f + 0.0f);  // -0 -> +0
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ unsigned long long pack_key(float key, int idx) {
+    return ((unsigned long long)order_bits(key) << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)idx);
+}
+__device__ __forceinline__ int unpack_idx(unsigned long long p) {
+    return (int)(0xFFFFFFFFu - (uint32_t)(p & 0xFFFFFFFFull));
+}
+
+template <int NPL>
+__device__ __forceinline__ float pick(const float (&v)[NPL], int j) {
+    float r = v[0];
+#pragma unroll
+    for (int q = 1; q < NPL; ++q) r = (q == j) ? v[q] : r;
+    return r;
+}
+
+// One round of argmax over the available entries; removes the winner and returns its index.
+template <int NPL>
+__device__ __forceinline__ int take_best(const float (&key)[NPL], bool (&avail)[NPL], int lane) {
+    unsigned long long best = 0;
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) {
+        unsigned long long p = avail[j] ? pack_key(key[j], lane + 64 * j) : 0ull;
+        best = p > best ? p : best;
+    }
+    best = wave_max_u64(best);
+    const int idx = unpack_idx(best);
+#pragma unroll
+    for (int j = 0; j < NPL; ++j)
+        if (lane + 64 * j == idx) avail[j] = false;
+    return idx;
+}
+
+template <int NPL>
+__global__ __launch_bounds__(256) void k_select(SelectArgs a) {
+    __shared__ float sh_key[4][NPL * 64];
+    const int lane = threadIdx.x & 63;
+    const int wv = threadIdx.x >> 6;
+    const int t_raw = blockIdx.x * 4 + wv;
+    const bool active = t_raw < a.T;
+    const int t = active ? t_raw : a.T - 1;
+    const int N = a.N;
+
+    float l[NPL], key[NPL], s[NPL];
+    bool avail[NPL];
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) {
+        const int i = lane + 64 * j;
+        const bool v = i < N;
+        l[j] = v ? a.logits[(size_t)t * N + i] : -INFINITY;
+        avail[j] = v;
+    }
+    float lmax = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) lmax = fmaxf(lmax, l[j]);
+    lmax = wave_max(lmax);
+    float z = 0.f;
+    if (a.gating == 1) {
+#pragma unroll
+        for (int j = 0; j < NPL; ++j) {
+            const int i = lane + 64 * j;
+            s[j] = 1.0f / (1.0f + expf(-l[j]));
+            key[j] = s[j] + ((a.bias && i < N) ? a.bias[i] : 0.0f);
+        }
+    } else {
+        // softmax modes rank by the logits (softmax is monotone)
+#pragma unroll
+        for (int j = 0; j < NPL; ++j) {
+            s[j] = (lane + 64 * j < N) ? expf(l[j] - lmax) : 0.0f;
+            key[j] = l[j];
+            z += s[j];
+        }
+        z = wave_sum(z);
+    }
+
+    if (a.n_group > 0) {
+        // group scores: sum of the keys of each contiguous group, in index order
+        // (softmax modes: the probabilities s, as ranked; sigmoid mode: s + b)
+#pragma unroll
+        for (int j = 0; j < NPL; ++j) sh_key[wv][lane + 64 * j] = a.gating == 1 ? key[j] : s[j] / z;
+        __syncthreads();
+        const int per = N / a.n_group;
+        float gs = -INFINITY;
+        if (lane < a.n_group) {
+            gs = 0.f;
+            for (int q = 0; q < per; ++q) gs += sh_key[wv][lane * per + q];
+        }
+        float gkey[1] = {gs};
+        bool gav[1] = {lane < a.n_group};
+        unsigned long long chosen = 0;
+        for (int r = 0; r < a.topk_group; ++r) chosen |= 1ull << take_best<1>(gkey, gav, lane);
+#pragma unroll
+        for (int j = 0; j < NPL; ++j) {
+            const int i = lane + 64 * j;
+            if (avail[j] && !((chosen >> (i / per)) & 1ull)) avail[j] = false;
+        }
+    }
+    for (int r = 0; r < a.mask_r; ++r) take_best<NPL>(key, avail, lane);
+
+    int my_idx = 0;
+    float my_l = 0.f, my_s = 0.f;
+    for (int k = 0; k < a.K; ++k) {
+        const int idx = take_best<NPL>(key, avail, lane);
+        const int j = idx >> 6;
+        const float wl = __shfl(pick<NPL>(l, j), idx & 63);
+        const float ws = __shfl(pick<NPL>(s, j), idx & 63);
+        if (lane == k) { my_idx = idx; my_l = wl; my_s = ws; }
+    }
+    const bool mine = lane < a.K;
+    float g;
+    if (a.gating == 0) {
+        g = my_s / z;
+    } else if (a.gating == 1) {
+        const float sum = wave_sum(mine ? my_s : 0.0f);
+        g = sum > 0.0f ? my_s / sum : 1.0f / (float)a.K;
+    } else {
+        const float m0 = __shfl(my_l, 0);
+        const float ex = mine ? expf(my_l - m0) : 0.0f;
+        g = ex / wave_sum(ex);
+    }
+    if (active && mine) {
+        a.topk_idx[(size_t)t * a.K + lane] = my_idx;
+        a.topk_w[(size_t)t * a.K + lane] = g;
+    }
+}
+
+hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
+    if (a.T == 0 || a.K == 0) return hipSuccess;
+    dim3 grid((a.T + 3) / 4), block(256);
+    const int npl = (a.N + 63) / 64;
+    if (npl <= 1) hipLaunchKernelGGL(k_select<1>, grid, block, 0, s, a);
+    else if (npl <= 2) hipLaunchKernelGGL(k_select<2>, grid, block, 0, s, a);
+    else if (npl <= 4) hipLaunchKernelGGL(k_select<4>, grid, block, 0, s, a);
+    else if (npl <= 8) hipLaunchKernelGGL(k_select<8>, grid, block, 0, s, a);
+    else hipLaunchKernelGGL(k_select<16>, grid, block, 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace moe

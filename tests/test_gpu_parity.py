@@ -1,0 +1,303 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle, stage by stage and whole layer.
+
+Small layers are compared on every token; they span several 128-row tiles, ragged tails in
+both GEMM dimensions, empty and overfull expert groups.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from parity_util import (Case, check_close, check_routing, gpu_shape, layer_parity, sample_tokens, say, to_dev,
+                         to_f64)
+from synth import (ACT_RELU_BIAS, ACT_SWIGLU, DT_BF16, DT_F32, GATE_SIGMOID_BIAS_NORM, GATE_SOFTMAX,
+                   GATE_SOFTMAX_RENORM, Workload)
+
+pytestmark = pytest.mark.gpu
+
+# T=300 rows -> 3 m-tiles with a ragged tail; H=320 -> a ragged 128-column tile in the down GEMM;
+# I=192 -> 3 SwiGLU column tiles.
+RAGGED = Workload("ragged", "ragged bf16 SwiGLU sigmoid+bias layer", 300, 320, 16, 3, 2, 192,
+                  GATE_SIGMOID_BIAS_NORM, ACT_SWIGLU, DT_BF16, bias_var=0.01)
+
+VARIANTS = {
+    "ragged": RAGGED,
+    "relu_softmax_bf16": RAGGED.with_(name="relu_softmax_bf16", gating=GATE_SOFTMAX, act=ACT_RELU_BIAS, bias_var=0.0,
+                                      I=256),
+    "swiglu_f32": RAGGED.with_(name="swiglu_f32", dtype=DT_F32, T=130),
+    "renorm_softmax": RAGGED.with_(name="renorm_softmax", gating=GATE_SOFTMAX_RENORM, bias_var=0.0),
+    "all_experts": RAGGED.with_(name="all_experts", K_r=16, Ks=1),
+    "no_shared": RAGGED.with_(name="no_shared", Ks=0, K_r=5),
+    "group_limited": RAGGED.with_(name="group_limited", N_r=32, K_r=4, n_group=8, topk_group=2),
+    "group_limited_softmax": RAGGED.with_(name="group_limited_softmax", N_r=32, K_r=4, n_group=4, topk_group=2,
+                                          gating=GATE_SOFTMAX, bias_var=0.0),
+    "mask_probe": RAGGED.with_(name="mask_probe", N_r=32, K_r=4, mask_top_r=2),
+    "many_experts": RAGGED.with_(name="many_experts", T=200, N_r=600, K_r=12, Ks=1, I=64, H=256),
+}
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import fine_grained_shared_amd as moe
+    moe.load()
+    return torch
+
+
+def test_c0_tiny_fp32_layer_every_token(torch_cuda):
+    case = Case(synth.WORKLOADS["c0"])
+    stats, _ = layer_parity(case, label="c0")
+    assert stats["fro_out"] <= 1e-5
+
+
+@pytest.mark.parametrize("name", list(VARIANTS))
+def test_layer_variants_every_token(torch_cuda, name):
+    case = Case(VARIANTS[name])
+    layer_parity(case, label=name)
+
+
+@pytest.mark.parametrize("name", ["c1a", "c1b", "c1b_iso", "c2"])
+def test_layer_configs_sampled(torch_cuda, name):
+    w = synth.WORKLOADS[name]
+    case = Case(w)
+    toks = sample_tokens(w.T, 96)
+    stats, (out, idx, wts) = layer_parity(case, tokens=toks, label=name)
+    # load histogram of the realised routing (c2: the 8 hot experts draw more tokens)
+    counts = np.bincount(idx.cpu().numpy().reshape(-1), minlength=w.N_r)
+    say("[parity] %s: load max/mean %.2f, empty %d" % (name, counts.max() / counts.mean(), (counts == 0).sum()))
+    if name == "c2":
+        assert counts[:8].mean() > counts[8:].mean()
+
+
+# ---------------------------------------------------------------- stages (ragged layer)
+
+@pytest.fixture(scope="module")
+def ragged(torch_cuda):
+    return Case(RAGGED)
+
+
+def test_stage_route(ragged, torch_cuda):
+    import fine_grained_shared_amd as moe
+    torch = torch_cuda
+    w, d = ragged.w, ragged.dev
+    s = gpu_shape(w)
+    idx = torch.empty((w.T, w.K_r), dtype=torch.int32, device="cuda")
+    wts = torch.empty((w.T, w.K_r), dtype=torch.float32, device="cuda")
+    moe.moe_route(s, d["u"], d["centroids"], d["bias"], idx, wts, moe.workspace(s))
+    torch.cuda.synchronize()
+    sel_o, g_o, gap = oracle.route(oracle.shape_of(w), ragged.inp["u"], ragged.inp["centroids"], ragged.inp["bias"])
+    check_routing(idx.cpu().numpy(), wts.cpu().numpy().astype(np.float64), sel_o, g_o, gap, "route")
+    # descending key order inside each token's list
+    sc = 1.0 / (1.0 + np.exp(-(synth.as_float64(ragged.inp["u"], DT_BF16) @
+                               synth.as_float64(ragged.inp["centroids"], DT_BF16).T)))
+    key = sc + ragged.inp["bias"].astype(np.float64)
+    kk = np.take_along_axis(key, idx.cpu().numpy().astype(np.int64), axis=1)
+    assert np.all(np.diff(kk, axis=1) <= 1e-6)
+
+
+def test_stage_dispatch_bit_exact(ragged, torch_cuda):
+    import fine_grained_shared_amd as moe
+    torch = torch_cuda
+    w, d = ragged.w, ragged.dev
+    s = gpu_shape(w)
+    ws = moe.workspace(s)
+    idx = torch.empty((w.T, w.K_r), dtype=torch.int32, device="cuda")
+    wts = torch.empty((w.T, w.K_r), dtype=torch.float32, device="cuda")
+    moe.moe_route(s, d["u"], d["centroids"], d["bias"], idx, wts, ws)
+    R = w.T * w.K_r
+    offsets = torch.full((w.N_r + 1,), -7, dtype=torch.int32, device="cuda")
+    row_token = torch.full((R,), -7, dtype=torch.int32, device="cuda")
+    pair_row = torch.full((R,), -7, dtype=torch.int32, device="cuda")
+    x_perm = torch.empty((R, w.H), dtype=torch.bfloat16, device="cuda")
+    moe.moe_dispatch(s, idx, offsets, row_token, pair_row, d["u"], x_perm, ws)
+    torch.cuda.synchronize()
+    o_ref, rt_ref, pr_ref = oracle.dispatch(idx.cpu().numpy(), w.N_r)
+    assert np.array_equal(offsets.cpu().numpy(), o_ref)
+    assert np.array_equal(row_token.cpu().numpy(), rt_ref)
+    assert np.array_equal(pair_row.cpu().numpy(), pr_ref)
+    assert torch.equal(x_perm, d["u"][row_token.long()])
+
+
+def test_stage_expert_ffn_both_gather_modes(ragged, torch_cuda):
+    import fine_grained_shared_amd as moe
+    torch = torch_cuda
+    w, d = ragged.w, ragged.dev
+    s = gpu_shape(w)
+    ws = moe.workspace(s)
+    R = w.T * w.K_r
+    idx = torch.empty((w.T, w.K_r), dtype=torch.int32, device="cuda")
+    wts = torch.empty((w.T, w.K_r), dtype=torch.float32, device="cuda")
+    moe.moe_route(s, d["u"], d["centroids"], d["bias"], idx, wts, ws)
+    offsets = torch.empty((w.N_r + 1,), dtype=torch.int32, device="cuda")
+    row_token = torch.empty((R,), dtype=torch.int32, device="cuda")
+    pair_row = torch.empty((R,), dtype=torch.int32, device="cuda")
+    x_perm = torch.empty((R, w.H), dtype=torch.bfloat16, device="cuda")
+    moe.moe_dispatch(s, idx, offsets, row_token, pair_row, d["u"], x_perm, ws)
+    y1 = torch.empty((R, w.H), dtype=torch.bfloat16, device="cuda")
+    y2 = torch.empty((R, w.H), dtype=torch.bfloat16, device="cuda")
+    moe.moe_expert_ffn(s, d["u"], row_token, offsets, d["w1"], None, d["w2"], y1, ws)
+    moe.moe_expert_ffn(s, x_perm, None, offsets, d["w1"], None, d["w2"], y2, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+    off = offsets.cpu().numpy()
+    rt = row_token.cpu().numpy()
+    uf = synth.as_float64(ragged.inp["u"], DT_BF16)
+    ref = np.zeros((R, w.H))
+    for e in range(w.N_r):
+        for r in range(off[e], off[e + 1]):
+            ref[r] = oracle.expert_ffn(w.H, w.I, w.act, w.dtype, ragged.inp["w1"][e], None, ragged.inp["w2"][e],
+                                       uf[rt[r]])
+    check_close(to_f64(y1), ref, DT_BF16, "expert_ffn")
+
+
+def test_stage_shared_ffn(ragged, torch_cuda):
+    import fine_grained_shared_amd as moe
+    torch = torch_cuda
+    w, d = ragged.w, ragged.dev
+    s = gpu_shape(w)
+    y = torch.empty((w.T, w.H), dtype=torch.bfloat16, device="cuda")
+    moe.moe_shared_ffn(s, d["u"], d["w1_sh"], None, d["w2_sh"], y, moe.workspace(s))
+    torch.cuda.synchronize()
+    uf = synth.as_float64(ragged.inp["u"], DT_BF16)
+    ref = np.zeros((w.T, w.H))
+    for t in range(w.T):
+        for j in range(w.Ks):
+            ref[t] += oracle.expert_ffn(w.H, w.I, w.act, w.dtype, ragged.inp["w1_sh"][j], None,
+                                        ragged.inp["w2_sh"][j], uf[t])
+    check_close(to_f64(y), ref, DT_BF16, "shared_ffn")
+
+
+@pytest.mark.parametrize("dtype", [DT_BF16, DT_F32])
+def test_stage_combine(torch_cuda, dtype):
+    import fine_grained_shared_amd as moe
+    torch = torch_cuda
+    T, H, K, N = 77, 192, 4, 9
+    rng = np.random.default_rng(3)
+    tdt = torch.bfloat16 if dtype == DT_BF16 else torch.float32
+    resid = torch.randn((T, H), generator=torch.Generator().manual_seed(1)).to(tdt).cuda()
+    ysh = torch.randn((T, H), generator=torch.Generator().manual_seed(2)).to(tdt).cuda()
+    yp = torch.randn((T * K, H), generator=torch.Generator().manual_seed(3)).to(tdt).cuda()
+    pr = torch.from_numpy(rng.permutation(T * K).astype(np.int32)).cuda()
+    g = torch.from_numpy(rng.random((T, K)).astype(np.float32)).cuda()
+    out = torch.empty((T, H), dtype=tdt, device="cuda")
+    s = moe.make_shape(T, H, N, K, 1, 64, 0, 1, dtype)
+    for use_res, use_sh in ((True, True), (False, True), (True, False)):
+        moe.moe_combine(s, resid if use_res else None, ysh if use_sh else None, yp, pr, g, out)
+        torch.cuda.synchronize()
+        ref = np.zeros((T, H))
+        if use_res:
+            ref += to_f64(resid)
+        if use_sh:
+            ref += to_f64(ysh)
+        ypf = to_f64(yp)
+        prn = pr.cpu().numpy().reshape(T, K)
+        gn = g.cpu().numpy().astype(np.float64)
+        for k in range(K):
+            ref += gn[:, k:k + 1] * ypf[prn[:, k]]
+        got = to_f64(out)
+        tol = 2.0 ** -8 if dtype == DT_BF16 else 1e-5
+        assert np.max(np.abs(got - ref) / (np.abs(ref) + 1e-3)) <= tol
+
+
+# ---------------------------------------------------------------- invariants and edge cases
+
+def test_token_permutation_and_batch_split_bit_exact(ragged, torch_cuda):
+    torch = torch_cuda
+    w = ragged.w
+    out, idx, wts = ragged.forward()
+    perm = torch.from_numpy(np.random.default_rng(5).permutation(w.T)).cuda()
+    up = ragged.dev["u"][perm].contiguous()
+    out_p, idx_p, _ = ragged.forward(u=up)
+    assert torch.equal(out_p, out[perm]) and torch.equal(idx_p, idx[perm])
+    h = 123
+    out_a, _, _ = ragged.forward(shape=gpu_shape(w, T=h), u=ragged.dev["u"][:h].contiguous())
+    out_b, _, _ = ragged.forward(shape=gpu_shape(w, T=w.T - h), u=ragged.dev["u"][h:].contiguous())
+    assert torch.equal(torch.cat([out_a, out_b]), out)
+    out2, idx2, wts2 = ragged.forward()
+    assert torch.equal(out2, out) and torch.equal(idx2, idx) and torch.equal(wts2, wts)
+
+
+def test_identity_when_no_experts(ragged, torch_cuda):
+    torch = torch_cuda
+    w = ragged.w.with_(K_r=0, Ks=0)
+    out, _, _ = ragged.forward(shape=gpu_shape(w))
+    assert torch.equal(out, ragged.dev["u"])
+    # K_r = 0 with shared experts: out = u + shared sum
+    w1 = ragged.w.with_(K_r=0)
+    case = Case(w1, ragged.inp)
+    layer_parity(case, label="kr0")
+
+
+def test_overfull_and_empty_groups(torch_cuda):
+    """A bias that forces every token onto experts 0..K_r-1: K_r groups of T rows, the rest empty."""
+    w = RAGGED.with_(name="forced", T=260)
+    inp = synth.make_inputs(w)
+    inp["bias"] = np.zeros(w.N_r, dtype=np.float32)
+    inp["bias"][: w.K_r] = 10.0
+    case = Case(w, inp)
+    _, (out, idx, wts) = layer_parity(case, label="forced")
+    assert np.array_equal(np.sort(idx.cpu().numpy(), axis=1), np.tile(np.arange(w.K_r), (w.T, 1)))
+
+
+@pytest.mark.parametrize("T", [0, 1, 2])
+def test_tiny_token_counts(torch_cuda, T):
+    torch = torch_cuda
+    case = Case(RAGGED.with_(T=max(T, 1)))
+    if T == 0:
+        out, idx, wts = case.forward(shape=gpu_shape(case.w, T=0), u=case.dev["u"][:0])
+        torch.cuda.synchronize()
+        assert out.shape == (0, case.w.H)
+        return
+    case = case.with_tokens(T)
+    layer_parity(case, label="T=%d" % T)
+
+
+def test_error_paths(ragged, torch_cuda):
+    import fine_grained_shared_amd as moe
+    torch = torch_cuda
+    w, d = ragged.w, ragged.dev
+    s = gpu_shape(w)
+    out = torch.empty((w.T, w.H), dtype=torch.bfloat16, device="cuda")
+    small = torch.empty(1024, dtype=torch.uint8, device="cuda")
+    with pytest.raises(moe.MoeError) as e:
+        moe.moe_layer_forward(s, d["u"], d["centroids"], d["bias"], d["w1"], None, d["w2"], d["w1_sh"], None,
+                              d["w2_sh"], 0, out, None, None, small)
+    assert e.value.status == moe.MOE_ERR_WORKSPACE
+    ws = moe.workspace(s)
+    flat = torch.empty(w.T * w.H + 1, dtype=torch.bfloat16, device="cuda")
+    mis = flat[1:].view(w.T, w.H)   # 2-byte misaligned
+    with pytest.raises(moe.MoeError) as e:
+        moe.moe_layer_forward(s, mis, d["centroids"], d["bias"], d["w1"], None, d["w2"], d["w1_sh"], None,
+                              d["w2_sh"], 0, out, None, None, ws)
+    assert e.value.status == moe.MOE_ERR_INVALID_ARG
+    with pytest.raises(moe.MoeError) as e:   # selection bias outside the sigmoid gating
+        moe.moe_layer_forward(gpu_shape(w, gating=GATE_SOFTMAX), d["u"], d["centroids"], d["bias"], d["w1"], None,
+                              d["w2"], d["w1_sh"], None, d["w2_sh"], 0, out, None, None, ws)
+    assert e.value.status == moe.MOE_ERR_INVALID_ARG
+
+
+def test_bias_update_bit_exact(ragged, torch_cuda):
+    import fine_grained_shared_amd as moe
+    torch = torch_cuda
+    w, d = ragged.w, ragged.dev
+    s = gpu_shape(w)
+    ws = moe.workspace(s)
+    R = w.T * w.K_r
+    idx = torch.empty((w.T, w.K_r), dtype=torch.int32, device="cuda")
+    wts = torch.empty((w.T, w.K_r), dtype=torch.float32, device="cuda")
+    bias = d["bias"].clone()
+    offsets = torch.empty((w.N_r + 1,), dtype=torch.int32, device="cuda")
+    row_token = torch.empty((R,), dtype=torch.int32, device="cuda")
+    pair_row = torch.empty((R,), dtype=torch.int32, device="cuda")
+    counts = torch.empty((w.N_r,), dtype=torch.int32, device="cuda")
+    b_host = ragged.inp["bias"].copy()
+    for step in range(3):
+        moe.moe_route(s, d["u"], d["centroids"], bias, idx, wts, ws)
+        moe.moe_dispatch(s, idx, offsets, row_token, pair_row, None, None, ws)
+        moe.moe_bias_update(s, offsets, 0.01, bias, counts)
+        torch.cuda.synchronize()
+        ref_counts = np.bincount(idx.cpu().numpy().reshape(-1), minlength=w.N_r)
+        assert np.array_equal(counts.cpu().numpy(), ref_counts)
+        b_host = oracle.bias_update(w.N_r, w.T, w.K_r, ref_counts, 0.01, b_host)
+        assert np.array_equal(bias.cpu().numpy(), b_host)
