@@ -190,8 +190,17 @@ int do_expert_ffn(const moe_shape* s, const void* x, const int32_t* row_token, c
     return MOE_OK;
 }
 
+// Shared experts.  With `comb` (bf16 only) the down GEMM's epilogue also adds the residual and the
+// gate-weighted routed rows and writes the layer output to y.
+struct Combine {
+    const void* resid;
+    const void* y_perm;
+    const int32_t* pair_row;
+    const float* topk_w;
+};
+
 int do_shared_ffn(const moe_shape* s, const void* x, const void* w1, const float* b1, const void* w2, void* y,
-                  void* act, hipStream_t st) {
+                  void* act, hipStream_t st, const Combine* comb = nullptr) {
     if (s->T == 0 || s->Ks == 0) return MOE_OK;
     const int n1 = s->act == MOE_ACT_SWIGLU ? 2 * s->I : s->I;
     moe::GemmParams up{};
@@ -232,7 +241,16 @@ int do_shared_ffn(const moe_shape* s, const void* x, const void* w1, const float
     dn.max_rows = s->T;
     dn.C = y;
     dn.ldc = s->H;
-    MOE_TRY(MOE_PROF_SHARED_DOWN, st, moe::launch_gemm(s->dtype, moe::GM_DOWN, dn, st));
+    if (comb) {
+        dn.resid = comb->resid;
+        dn.y_perm = comb->y_perm;
+        dn.pair_row = comb->pair_row;
+        dn.topk_w = comb->topk_w;
+        dn.K_r = s->K_r;
+        dn.R = (long long)s->T * s->K_r;
+    }
+    MOE_TRY(MOE_PROF_SHARED_DOWN, st,
+            moe::launch_gemm(s->dtype, comb ? moe::GM_DOWN_COMBINE : moe::GM_DOWN, dn, st));
     return MOE_OK;
 }
 
@@ -354,12 +372,19 @@ int moe_layer_forward(const moe_shape* s, const void* u, const void* centroids, 
                                 at<int32_t>(ws, L.tiles), at<void>(ws, L.act), st)) != MOE_OK)
             return rc;
     }
+    const void* resid = (flags & MOE_FLAG_NO_RESIDUAL) ? nullptr : u;
+    if (s->Ks > 0 && s->dtype == MOE_BF16) {
+        // combine fused into the shared experts' down GEMM: the shared output never leaves the
+        // fp32 accumulators, and the layer output is written once
+        const Combine comb{resid, y_perm, pair_row, wts};
+        return do_shared_ffn(s, u, w1_sh, b1_sh, w2_sh, out, at<void>(ws, L.act_sh), st, &comb);
+    }
     if (s->Ks > 0) {
         if ((rc = do_shared_ffn(s, u, w1_sh, b1_sh, w2_sh, y_sh, at<void>(ws, L.act_sh), st)) != MOE_OK) return rc;
     }
     MOE_TRY(MOE_PROF_COMBINE, st,
-            moe::launch_combine(s->dtype, (flags & MOE_FLAG_NO_RESIDUAL) ? nullptr : u, s->Ks > 0 ? y_sh : nullptr,
-                                y_perm, pair_row, wts, out, s->T, s->H, s->K_r, st));
+            moe::launch_combine(s->dtype, resid, s->Ks > 0 ? y_sh : nullptr, y_perm, pair_row, wts, out, s->T, s->H,
+                                s->K_r, st));
     return MOE_OK;
 }
 

@@ -96,10 +96,15 @@ __device__ __forceinline__ bool decode_tile(const GemmParams& p, int NT, int bm,
 }
 
 // ---------------------------------------------------------------- bf16 MFMA grouped GEMM
+constexpr int EPW = BN + 4;  // fp32 staging row of the LDS epilogue (floats)
+constexpr int kSmemBytes = 2 * (BM + BN) * LDSW * 2;
+static_assert(BM * EPW * 4 <= kSmemBytes, "epilogue staging must fit in the operand buffers");
+
 template <int MODE>
 __global__ __launch_bounds__(256, 2) void k_gemm_bf16(GemmParams p, int NT) {
-    __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM][LDSW];
-    __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN][LDSW];
+    __shared__ __attribute__((aligned(16))) unsigned char smem[kSmemBytes];
+    auto sA = reinterpret_cast<uint16_t(*)[BM][LDSW]>(smem);
+    auto sB = reinterpret_cast<uint16_t(*)[BN][LDSW]>(smem + 2 * BM * LDSW * 2);
 
     const int L = xcd_remap(blockIdx.x, gridDim.x);
     TileInfo ti;
@@ -188,6 +193,65 @@ __global__ __launch_bounds__(256, 2) void k_gemm_bf16(GemmParams p, int NT) {
 
     // epilogue.  D[i][j] of a 32x32 block: column j = lane % 32,
     // row i = 8 * (q / 4) + 4 * (lane / 32) + (q % 4) for accumulator element q.
+    if (MODE == GM_DOWN || MODE == GM_DOWN_COMBINE) {
+        // Stage the fp32 tile through LDS, then let 16 threads cover each row with 16-byte
+        // vectors (coalesced stores; the combine reads whole 16-byte pieces of routed rows).
+        float* st = reinterpret_cast<float*>(smem);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                    const int rl = wm * 64 + i * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+                    st[rl * EPW + wn * 64 + j * 32 + (lane & 31)] = acc[i][j][q];
+                }
+        __syncthreads();
+        const int cq = (tid & 15) * 8;
+        const int col0 = ti.nt * BN + cq;
+        if (col0 >= p.N) return;
+        uint16_t* C = (uint16_t*)p.C;
+#pragma unroll 1
+        for (int pr = 0; pr < BM / 16; ++pr) {
+            const int rl = (tid >> 4) + 16 * pr;
+            if (rl >= ti.rows) break;
+            const float4 v0 = *reinterpret_cast<const float4*>(&st[rl * EPW + cq]);
+            const float4 v1 = *reinterpret_cast<const float4*>(&st[rl * EPW + cq + 4]);
+            float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+            const long long row = ti.row0 + rl;
+            if (MODE == GM_DOWN_COMBINE) {
+                // fixed order: residual, shared experts, then k = 0 .. K_r-1
+                if (p.resid) {
+                    const uint4 q = *reinterpret_cast<const uint4*>((const uint16_t*)p.resid + row * p.N + col0);
+                    const uint32_t wv[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        v[2 * e] = __uint_as_float(wv[e] << 16) + v[2 * e];
+                        v[2 * e + 1] = __uint_as_float(wv[e] & 0xFFFF0000u) + v[2 * e + 1];
+                    }
+                }
+                for (int k = 0; k < p.K_r; ++k) {
+                    long long pr_row = (long long)(uint32_t)p.pair_row[row * p.K_r + k];
+                    pr_row = pr_row < p.R ? pr_row : p.R - 1;
+                    const float g = p.topk_w[row * p.K_r + k];
+                    const uint4 q = *reinterpret_cast<const uint4*>((const uint16_t*)p.y_perm + pr_row * p.N + col0);
+                    const uint32_t wv[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        v[2 * e] = fmaf(g, __uint_as_float(wv[e] << 16), v[2 * e]);
+                        v[2 * e + 1] = fmaf(g, __uint_as_float(wv[e] & 0xFFFF0000u), v[2 * e + 1]);
+                    }
+                }
+            }
+            uint4 o;
+            o.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+            o.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+            o.z = (uint32_t)f32_to_bf16(v[4]) | ((uint32_t)f32_to_bf16(v[5]) << 16);
+            o.w = (uint32_t)f32_to_bf16(v[6]) | ((uint32_t)f32_to_bf16(v[7]) << 16);
+            *reinterpret_cast<uint4*>(C + row * p.ldc + col0) = o;
+        }
+        return;
+    }
     uint16_t* C = (uint16_t*)p.C;
     const long long coff = p.offsets ? 0 : (long long)ti.g * p.sC_group;
 #pragma unroll
@@ -277,6 +341,7 @@ __global__ __launch_bounds__(256) void k_gemm_f32(GemmParams p) {
 hipError_t launch_gemm(int dtype, int mode, const GemmParams& p, hipStream_t s) {
     if (p.G == 0 || p.max_rows == 0 || p.N == 0) return hipSuccess;
     if (dtype == 0) {
+        if (mode == GM_DOWN_COMBINE) return hipErrorInvalidValue;  // fp32 layers combine separately
         dim3 grid((p.N + 63) / 64, (p.max_rows + 3) / 4, p.offsets ? 1 : p.G);
         if (mode == GM_UP_SWIGLU) hipLaunchKernelGGL(k_gemm_f32<GM_UP_SWIGLU>, grid, dim3(256), 0, s, p);
         else if (mode == GM_UP_RELU) hipLaunchKernelGGL(k_gemm_f32<GM_UP_RELU>, grid, dim3(256), 0, s, p);
@@ -284,6 +349,7 @@ hipError_t launch_gemm(int dtype, int mode, const GemmParams& p, hipStream_t s) 
         return hipGetLastError();
     }
     const int NT = mode == GM_UP_SWIGLU ? (p.N + 63) / 64 : (p.N + BN - 1) / BN;
+    if (mode == GM_DOWN_COMBINE && p.offsets) return hipErrorInvalidValue;  // dense (shared) groups only
     long long mt;
     if (p.offsets) mt = (p.max_rows + BM - 1) / BM + p.G;  // sum of ceil(rows_g / BM) <= this
     else mt = (long long)p.G * ((p.M_dense + BM - 1) / BM);
@@ -292,7 +358,8 @@ hipError_t launch_gemm(int dtype, int mode, const GemmParams& p, hipStream_t s) 
     if (nb > 0x7FFFFFF8LL) return hipErrorInvalidValue;
     if (mode == GM_UP_SWIGLU) hipLaunchKernelGGL(k_gemm_bf16<GM_UP_SWIGLU>, dim3((unsigned)nb), dim3(256), 0, s, p, NT);
     else if (mode == GM_UP_RELU) hipLaunchKernelGGL(k_gemm_bf16<GM_UP_RELU>, dim3((unsigned)nb), dim3(256), 0, s, p, NT);
-    else hipLaunchKernelGGL(k_gemm_bf16<GM_DOWN>, dim3((unsigned)nb), dim3(256), 0, s, p, NT);
+    else if (mode == GM_DOWN) hipLaunchKernelGGL(k_gemm_bf16<GM_DOWN>, dim3((unsigned)nb), dim3(256), 0, s, p, NT);
+    else hipLaunchKernelGGL(k_gemm_bf16<GM_DOWN_COMBINE>, dim3((unsigned)nb), dim3(256), 0, s, p, NT);
     return hipGetLastError();
 }
 

@@ -32,7 +32,9 @@ hipError_t launch_gather(int dtype, const void* u, const int32_t* row_token, int
                          hipStream_t s);
 
 // ---------------------------------------------------------------- expert FFN (grouped GEMM)
-enum { GM_UP_SWIGLU = 0, GM_UP_RELU = 1, GM_DOWN = 2 };
+// GM_DOWN_COMBINE: the shared experts' down GEMM whose epilogue also adds the residual and the
+// gate-weighted routed rows (Eq. 9) and writes the layer output.
+enum { GM_UP_SWIGLU = 0, GM_UP_RELU = 1, GM_DOWN = 2, GM_DOWN_COMBINE = 3 };
 
 struct GemmParams {
     const void* A;            // activation rows
@@ -57,6 +59,13 @@ struct GemmParams {
     long long sC_group;       // dense mode: column offset of group g in C is g * sC_group
     const float* bias;        // ReLU bias [G, N] (NULL = 0)
     long long sbias_group;
+    // GM_DOWN_COMBINE only: out[t] = resid[t] + C_acc[t] + sum_k topk_w[t,k] * y_perm[pair_row[t,k]]
+    const void* resid;        // [M_dense, N] or NULL
+    const void* y_perm;       // [R, N]
+    const int32_t* pair_row;  // [M_dense, K_r]
+    const float* topk_w;      // [M_dense, K_r]
+    int K_r;
+    long long R;
 };
 // m-tile prefix of the groups defined by offsets (grouped mode), for tiles of bm rows
 hipError_t launch_tile_plan(const int32_t* offsets, int G, int bm, int32_t* tiles, hipStream_t s);

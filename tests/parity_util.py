@@ -94,7 +94,10 @@ def check_routing(sel_gpu, w_gpu, sel_orc, g_orc, gap, label=""):
     return int(near.sum())
 
 
-def check_close(got, ref, dtype, label=""):
+def check_close(got, ref, dtype, label="", output_rounding=False):
+    """Relative Frobenius and max-abs checks.  output_rounding: the compared tensor is itself a
+    bf16 output of a different quantity than the bar was set for (the MoE-only part); each
+    element may then also differ by its own bf16 rounding, at most 2^-8 |ref|."""
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     assert got.shape == ref.shape, (got.shape, ref.shape)
@@ -105,9 +108,14 @@ def check_close(got, ref, dtype, label=""):
         assert fro <= F32_FRO, "%s: rel Frobenius %g > %g" % (label, fro, F32_FRO)
     else:
         rms = den / np.sqrt(max(ref.size, 1))
-        mx = np.abs(got - ref).max() if ref.size else 0.0
+        err = np.abs(got - ref)
+        allow = BF16_MAX * rms + (2.0 ** -8 * np.abs(ref) if output_rounding else 0.0)
+        excess = (err - allow).max() if ref.size else -1.0
+        mx = err.max() if ref.size else 0.0
+        say("[check] %s: rel Frobenius %.3e, max abs %.3e = %.4f rms" % (label, fro, mx, mx / max(rms, 1e-300)))
         assert fro <= BF16_FRO, "%s: rel Frobenius %g > %g" % (label, fro, BF16_FRO)
-        assert mx <= BF16_MAX * rms, "%s: max abs %g > %g * rms %g" % (label, mx, BF16_MAX, rms)
+        assert excess <= 0.0, "%s: max abs %g beyond %g * rms %g%s" % (
+            label, mx, BF16_MAX, rms, " + 2^-8 |ref|" if output_rounding else "")
     return fro
 
 
@@ -149,6 +157,7 @@ def layer_parity(case, tokens=None, route_all=True, label=""):
     ref, _, _, _ = oracle.layer(s, case.inp, tokens=tok, forced_sel=forced)
     ref_moe, _, _, _ = oracle.layer(s, case.inp, tokens=tok, forced_sel=forced, residual=False)
     stats["fro_out"] = check_close(to_f64(out)[tok], ref, w.dtype, label + " out")
-    stats["fro_moe"] = check_close(to_f64(moe_part)[tok], ref_moe, w.dtype, label + " moe part")
+    stats["fro_moe"] = check_close(to_f64(moe_part)[tok], ref_moe, w.dtype, label + " moe part",
+                                   output_rounding=True)
     say("[parity] %s: ok %s" % (label or w.name, stats))
     return stats, (out, idx, wts)
