@@ -144,52 +144,73 @@ __global__ __launch_bounds__(256, 2) void k_gemm_bf16(GemmParams p, int NT) {
 #pragma unroll
             for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
-    uint4 ra[4], rb[4];
-    auto gload = [&](int kt) {
-        const int k = kt * BK;
-        const int seg = k / p.Kseg;
-        const long long boff = (long long)seg * p.sB_seg + (k - seg * p.Kseg);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            ra[i] = *reinterpret_cast<const uint4*>(ag[i] + k);
-            rb[i] = *reinterpret_cast<const uint4*>(bg[i] + boff);
-        }
-    };
-    auto sstore = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            *reinterpret_cast<uint4*>(&sA[buf][lr + 32 * i][kc]) = ra[i];
-            *reinterpret_cast<uint4*>(&sB[buf][lr + 32 * i][kc]) = rb[i];
-        }
-    };
-    auto brow = [&](int j) { return MODE == GM_UP_SWIGLU ? j * 64 + wn * 32 : wn * 64 + j * 32; };
-
     const int nk = p.K / BK;
-    gload(0);
-    sstore(0);
+    // B offset of k-tile kt inside the (possibly segmented) reduction
+#define MOE_BOFF(kt) ((long long)(((kt) * BK) / p.Kseg) * p.sB_seg + (((kt) * BK) % p.Kseg))
+    uint4 ra0, ra1, ra2, ra3, rb0, rb1, rb2, rb3;
+    {
+        const long long bo = MOE_BOFF(0);
+        ra0 = *reinterpret_cast<const uint4*>(ag[0]);
+        ra1 = *reinterpret_cast<const uint4*>(ag[1]);
+        ra2 = *reinterpret_cast<const uint4*>(ag[2]);
+        ra3 = *reinterpret_cast<const uint4*>(ag[3]);
+        rb0 = *reinterpret_cast<const uint4*>(bg[0] + bo);
+        rb1 = *reinterpret_cast<const uint4*>(bg[1] + bo);
+        rb2 = *reinterpret_cast<const uint4*>(bg[2] + bo);
+        rb3 = *reinterpret_cast<const uint4*>(bg[3] + bo);
+    }
+    *reinterpret_cast<uint4*>(&sA[0][lr][kc]) = ra0;
+    *reinterpret_cast<uint4*>(&sA[0][lr + 32][kc]) = ra1;
+    *reinterpret_cast<uint4*>(&sA[0][lr + 64][kc]) = ra2;
+    *reinterpret_cast<uint4*>(&sA[0][lr + 96][kc]) = ra3;
+    *reinterpret_cast<uint4*>(&sB[0][lr][kc]) = rb0;
+    *reinterpret_cast<uint4*>(&sB[0][lr + 32][kc]) = rb1;
+    *reinterpret_cast<uint4*>(&sB[0][lr + 64][kc]) = rb2;
+    *reinterpret_cast<uint4*>(&sB[0][lr + 96][kc]) = rb3;
     __syncthreads();
+    const int br0 = MODE == GM_UP_SWIGLU ? wn * 32 : wn * 64;
+    const int br1 = MODE == GM_UP_SWIGLU ? 64 + wn * 32 : wn * 64 + 32;
     for (int kt = 0; kt < nk; ++kt) {
         const int buf = kt & 1;
-        if (kt + 1 < nk) gload(kt + 1);
+        // prefetch the next k-tile (the last iteration re-reads the current one: no branch,
+        // so the staging registers stay registers)
+        const int kn = kt + 1 < nk ? kt + 1 : kt;
+        {
+            const int k = kn * BK;
+            const long long bo = MOE_BOFF(kn);
+            ra0 = *reinterpret_cast<const uint4*>(ag[0] + k);
+            ra1 = *reinterpret_cast<const uint4*>(ag[1] + k);
+            ra2 = *reinterpret_cast<const uint4*>(ag[2] + k);
+            ra3 = *reinterpret_cast<const uint4*>(ag[3] + k);
+            rb0 = *reinterpret_cast<const uint4*>(bg[0] + bo);
+            rb1 = *reinterpret_cast<const uint4*>(bg[1] + bo);
+            rb2 = *reinterpret_cast<const uint4*>(bg[2] + bo);
+            rb3 = *reinterpret_cast<const uint4*>(bg[3] + bo);
+        }
 #pragma unroll
         for (int s = 0; s < BK / 16; ++s) {
             const int ko = s * 16 + (lane >> 5) * 8;
-            bf16x8 af[2], bfr[2];
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-                af[i] = *reinterpret_cast<const bf16x8*>(&sA[buf][wm * 64 + i * 32 + (lane & 31)][ko]);
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-                bfr[j] = *reinterpret_cast<const bf16x8*>(&sB[buf][brow(j) + (lane & 31)][ko]);
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+            const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(&sA[buf][wm * 64 + (lane & 31)][ko]);
+            const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(&sA[buf][wm * 64 + 32 + (lane & 31)][ko]);
+            const bf16x8 b0 = *reinterpret_cast<const bf16x8*>(&sB[buf][br0 + (lane & 31)][ko]);
+            const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(&sB[buf][br1 + (lane & 31)][ko]);
+            acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, acc[0][0], 0, 0, 0);
+            acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b1, acc[0][1], 0, 0, 0);
+            acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b0, acc[1][0], 0, 0, 0);
+            acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, acc[1][1], 0, 0, 0);
         }
-        if (kt + 1 < nk) sstore(buf ^ 1);
+        const int nb = buf ^ 1;
+        *reinterpret_cast<uint4*>(&sA[nb][lr][kc]) = ra0;
+        *reinterpret_cast<uint4*>(&sA[nb][lr + 32][kc]) = ra1;
+        *reinterpret_cast<uint4*>(&sA[nb][lr + 64][kc]) = ra2;
+        *reinterpret_cast<uint4*>(&sA[nb][lr + 96][kc]) = ra3;
+        *reinterpret_cast<uint4*>(&sB[nb][lr][kc]) = rb0;
+        *reinterpret_cast<uint4*>(&sB[nb][lr + 32][kc]) = rb1;
+        *reinterpret_cast<uint4*>(&sB[nb][lr + 64][kc]) = rb2;
+        *reinterpret_cast<uint4*>(&sB[nb][lr + 96][kc]) = rb3;
         __syncthreads();
     }
+#undef MOE_BOFF
 
     // epilogue.  D[i][j] of a 32x32 block: column j = lane % 32,
     // row i = 8 * (q / 4) + 4 * (lane / 32) + (q % 4) for accumulator element q.

@@ -103,28 +103,28 @@ __device__ __forceinline__ int unpack_idx(unsigned long long p) {
     return (int)(0xFFFFFFFFu - (uint32_t)(p & 0xFFFFFFFFull));
 }
 
+// One round of argmax over the entries whose bit is set in `avail` (bit j: expert lane + 64 j);
+// clears the winner's bit in its owner lane and returns the winner's index.  The winner's
+// values of v0 and v1 are broadcast into w0 and w1 (tracked alongside the key, so no
+// register array is indexed dynamically).
 template <int NPL>
-__device__ __forceinline__ float pick(const float (&v)[NPL], int j) {
-    float r = v[0];
-#pragma unroll
-    for (int q = 1; q < NPL; ++q) r = (q == j) ? v[q] : r;
-    return r;
-}
-
-// One round of argmax over the available entries; removes the winner and returns its index.
-template <int NPL>
-__device__ __forceinline__ int take_best(const float (&key)[NPL], bool (&avail)[NPL], int lane) {
+__device__ __forceinline__ int take_best(const float (&key)[NPL], uint32_t& avail, int lane, const float (&v0)[NPL],
+                                         const float (&v1)[NPL], float& w0, float& w1) {
     unsigned long long best = 0;
+    float b0 = 0.f, b1 = 0.f;
 #pragma unroll
     for (int j = 0; j < NPL; ++j) {
-        unsigned long long p = avail[j] ? pack_key(key[j], lane + 64 * j) : 0ull;
-        best = p > best ? p : best;
+        const unsigned long long p = ((avail >> j) & 1u) ? pack_key(key[j], lane + 64 * j) : 0ull;
+        const bool better = p > best;
+        best = better ? p : best;
+        b0 = better ? v0[j] : b0;
+        b1 = better ? v1[j] : b1;
     }
     best = wave_max_u64(best);
     const int idx = unpack_idx(best);
-#pragma unroll
-    for (int j = 0; j < NPL; ++j)
-        if (lane + 64 * j == idx) avail[j] = false;
+    if ((idx & 63) == lane) avail &= ~(1u << (idx >> 6));
+    w0 = __shfl(b0, idx & 63);
+    w1 = __shfl(b1, idx & 63);
     return idx;
 }
 
@@ -139,13 +139,13 @@ __global__ __launch_bounds__(256) void k_select(SelectArgs a) {
     const int N = a.N;
 
     float l[NPL], key[NPL], s[NPL];
-    bool avail[NPL];
+    uint32_t avail = 0;
 #pragma unroll
     for (int j = 0; j < NPL; ++j) {
         const int i = lane + 64 * j;
         const bool v = i < N;
         l[j] = v ? a.logits[(size_t)t * N + i] : -INFINITY;
-        avail[j] = v;
+        avail |= (v ? 1u : 0u) << j;
     }
     float lmax = -INFINITY;
 #pragma unroll
@@ -183,24 +183,23 @@ __global__ __launch_bounds__(256) void k_select(SelectArgs a) {
             for (int q = 0; q < per; ++q) gs += sh_key[wv][lane * per + q];
         }
         float gkey[1] = {gs};
-        bool gav[1] = {lane < a.n_group};
+        uint32_t gav = lane < a.n_group ? 1u : 0u;
         unsigned long long chosen = 0;
-        for (int r = 0; r < a.topk_group; ++r) chosen |= 1ull << take_best<1>(gkey, gav, lane);
+        float d0, d1;
+        for (int r = 0; r < a.topk_group; ++r) chosen |= 1ull << take_best<1>(gkey, gav, lane, gkey, gkey, d0, d1);
 #pragma unroll
         for (int j = 0; j < NPL; ++j) {
             const int i = lane + 64 * j;
-            if (avail[j] && !((chosen >> (i / per)) & 1ull)) avail[j] = false;
+            if (!((chosen >> (i / per)) & 1ull)) avail &= ~(1u << j);
         }
     }
-    for (int r = 0; r < a.mask_r; ++r) take_best<NPL>(key, avail, lane);
+    float wl, ws;
+    for (int r = 0; r < a.mask_r; ++r) take_best<NPL>(key, avail, lane, l, s, wl, ws);
 
     int my_idx = 0;
     float my_l = 0.f, my_s = 0.f;
     for (int k = 0; k < a.K; ++k) {
-        const int idx = take_best<NPL>(key, avail, lane);
-        const int j = idx >> 6;
-        const float wl = __shfl(pick<NPL>(l, j), idx & 63);
-        const float ws = __shfl(pick<NPL>(s, j), idx & 63);
+        const int idx = take_best<NPL>(key, avail, lane, l, s, wl, ws);
         if (lane == k) { my_idx = idx; my_l = wl; my_s = ws; }
     }
     const bool mine = lane < a.K;
