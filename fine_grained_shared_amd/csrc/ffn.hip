@@ -20,6 +20,19 @@ constexpr int LDSW = BK + 8;  // padded LDS row (elements)
 
 int gemm_bm(int dtype) { return dtype == 0 ? 1 : BM; }
 
+// Compute units of the current device (cached per device id).
+static int device_cus() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
 // ---------------------------------------------------------------- tile plan
 // tiles[g] = sum_{g' < g} ceil(rows(g') / bm); tiles[G] = total m-tiles.  One workgroup, G <= 1024.
 __global__ __launch_bounds__(1024) void k_tile_plan(const int32_t* __restrict__ offsets, int G, int bm,
@@ -96,20 +109,90 @@ __device__ __forceinline__ bool decode_tile(const GemmParams& p, int NT, int bm,
 }
 
 // ---------------------------------------------------------------- bf16 MFMA grouped GEMM
-constexpr int EPW = BN + 4;  // fp32 staging row of the LDS epilogue (floats)
+// Persistent: the grid holds two workgroups per CU; the workgroups of one XCD walk a
+// contiguous range of the tile list (so concurrently running tiles of an XCD share weight
+// and activation tiles in its L2), strided by the number of workgroups on that XCD.
+// Pipeline: k-tile kt+2 is fetched into registers while k-tile kt is multiplied out of LDS
+// and k-tile kt+1 waits in the other register set, so each global load has two iterations
+// to arrive.  Epilogues stage the fp32 tile through LDS and store 16-byte vectors.
+constexpr int EPW = BN + 4;  // fp32 staging row (floats)
 constexpr int kSmemBytes = 2 * (BM + BN) * LDSW * 2;
 static_assert(BM * EPW * 4 <= kSmemBytes, "epilogue staging must fit in the operand buffers");
 
+// Global -> register staging of one k-tile (4 A rows and 4 weight rows of 16 bytes per
+// thread), and register -> LDS.  Macros over named registers keep the staging in VGPRs.
+#define MOE_STAGE_DECL(S) uint4 S##a0, S##a1, S##a2, S##a3, S##b0, S##b1, S##b2, S##b3
+#define MOE_STAGE_LOAD(S, k, bo)                                   \
+    do {                                                           \
+        S##a0 = *reinterpret_cast<const uint4*>(ag0 + (k));        \
+        S##a1 = *reinterpret_cast<const uint4*>(ag1 + (k));        \
+        S##a2 = *reinterpret_cast<const uint4*>(ag2 + (k));        \
+        S##a3 = *reinterpret_cast<const uint4*>(ag3 + (k));        \
+        S##b0 = *reinterpret_cast<const uint4*>(bg0 + (bo));       \
+        S##b1 = *reinterpret_cast<const uint4*>(bg1 + (bo));       \
+        S##b2 = *reinterpret_cast<const uint4*>(bg2 + (bo));       \
+        S##b3 = *reinterpret_cast<const uint4*>(bg3 + (bo));       \
+    } while (0)
+#define MOE_STAGE_STORE(S, buf)                                            \
+    do {                                                                   \
+        *reinterpret_cast<uint4*>(&sA[buf][lr][kc]) = S##a0;              \
+        *reinterpret_cast<uint4*>(&sA[buf][lr + 32][kc]) = S##a1;         \
+        *reinterpret_cast<uint4*>(&sA[buf][lr + 64][kc]) = S##a2;         \
+        *reinterpret_cast<uint4*>(&sA[buf][lr + 96][kc]) = S##a3;         \
+        *reinterpret_cast<uint4*>(&sB[buf][lr][kc]) = S##b0;              \
+        *reinterpret_cast<uint4*>(&sB[buf][lr + 32][kc]) = S##b1;         \
+        *reinterpret_cast<uint4*>(&sB[buf][lr + 64][kc]) = S##b2;         \
+        *reinterpret_cast<uint4*>(&sB[buf][lr + 96][kc]) = S##b3;         \
+    } while (0)
+
+__device__ __forceinline__ void mma_tile(f32x16& c00, f32x16& c01, f32x16& c10, f32x16& c11,
+                                         const uint16_t (*sa)[LDSW], const uint16_t (*sb)[LDSW], int arow, int br0,
+                                         int br1, int lane) {
+#pragma unroll
+    for (int s = 0; s < BK / 16; ++s) {
+        const int ko = s * 16 + (lane >> 5) * 8;
+        const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(&sa[arow + (lane & 31)][ko]);
+        const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(&sa[arow + 32 + (lane & 31)][ko]);
+        const bf16x8 b0 = *reinterpret_cast<const bf16x8*>(&sb[br0 + (lane & 31)][ko]);
+        const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(&sb[br1 + (lane & 31)][ko]);
+        c00 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, c00, 0, 0, 0);
+        c01 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b1, c01, 0, 0, 0);
+        c10 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b0, c10, 0, 0, 0);
+        c11 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, c11, 0, 0, 0);
+    }
+}
+
+__device__ __forceinline__ uint4 pack8_bf16(const float (&v)[8]) {
+    uint4 o;
+    o.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+    o.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+    o.z = (uint32_t)f32_to_bf16(v[4]) | ((uint32_t)f32_to_bf16(v[5]) << 16);
+    o.w = (uint32_t)f32_to_bf16(v[6]) | ((uint32_t)f32_to_bf16(v[7]) << 16);
+    return o;
+}
+
+__device__ __forceinline__ void add8_bf16(float (&v)[8], uint4 q) {
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        v[2 * e] += __uint_as_float(w[e] << 16);
+        v[2 * e + 1] += __uint_as_float(w[e] & 0xFFFF0000u);
+    }
+}
+
+__device__ __forceinline__ void fma8_bf16(float (&v)[8], float g, uint4 q) {
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        v[2 * e] = fmaf(g, __uint_as_float(w[e] << 16), v[2 * e]);
+        v[2 * e + 1] = fmaf(g, __uint_as_float(w[e] & 0xFFFF0000u), v[2 * e + 1]);
+    }
+}
+
 template <int MODE>
-__global__ __launch_bounds__(256, 2) void k_gemm_bf16(GemmParams p, int NT) {
-    __shared__ __attribute__((aligned(16))) unsigned char smem[kSmemBytes];
+__device__ __forceinline__ void gemm_tile(const GemmParams& p, const TileInfo& ti, unsigned char* smem) {
     auto sA = reinterpret_cast<uint16_t(*)[BM][LDSW]>(smem);
     auto sB = reinterpret_cast<uint16_t(*)[BN][LDSW]>(smem + 2 * BM * LDSW * 2);
-
-    const int L = xcd_remap(blockIdx.x, gridDim.x);
-    TileInfo ti;
-    if (!decode_tile(p, NT, BM, L, ti)) return;
-
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
     const int lr = tid >> 3;       // 0..31: row handled by this thread in each 32-row slab
@@ -135,170 +218,147 @@ __global__ __launch_bounds__(256, 2) void k_gemm_bf16(GemmParams p, int NT) {
         }
         bg[i] = Bg + (size_t)wr * p.ldb + kc;
     }
+    const uint16_t *ag0 = ag[0], *ag1 = ag[1], *ag2 = ag[2], *ag3 = ag[3];
+    const uint16_t *bg0 = bg[0], *bg1 = bg[1], *bg2 = bg[2], *bg3 = bg[3];
 
-    f32x16 acc[2][2];
+    f32x16 c00, c01, c10, c11;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+    for (int q = 0; q < 16; ++q) {
+        c00[q] = 0.f;
+        c01[q] = 0.f;
+        c10[q] = 0.f;
+        c11[q] = 0.f;
+    }
 
     const int nk = p.K / BK;
-    // B offset of k-tile kt inside the (possibly segmented) reduction
-#define MOE_BOFF(kt) ((long long)(((kt) * BK) / p.Kseg) * p.sB_seg + (((kt) * BK) % p.Kseg))
-    uint4 ra0, ra1, ra2, ra3, rb0, rb1, rb2, rb3;
-    {
-        const long long bo = MOE_BOFF(0);
-        ra0 = *reinterpret_cast<const uint4*>(ag[0]);
-        ra1 = *reinterpret_cast<const uint4*>(ag[1]);
-        ra2 = *reinterpret_cast<const uint4*>(ag[2]);
-        ra3 = *reinterpret_cast<const uint4*>(ag[3]);
-        rb0 = *reinterpret_cast<const uint4*>(bg[0] + bo);
-        rb1 = *reinterpret_cast<const uint4*>(bg[1] + bo);
-        rb2 = *reinterpret_cast<const uint4*>(bg[2] + bo);
-        rb3 = *reinterpret_cast<const uint4*>(bg[3] + bo);
-    }
-    *reinterpret_cast<uint4*>(&sA[0][lr][kc]) = ra0;
-    *reinterpret_cast<uint4*>(&sA[0][lr + 32][kc]) = ra1;
-    *reinterpret_cast<uint4*>(&sA[0][lr + 64][kc]) = ra2;
-    *reinterpret_cast<uint4*>(&sA[0][lr + 96][kc]) = ra3;
-    *reinterpret_cast<uint4*>(&sB[0][lr][kc]) = rb0;
-    *reinterpret_cast<uint4*>(&sB[0][lr + 32][kc]) = rb1;
-    *reinterpret_cast<uint4*>(&sB[0][lr + 64][kc]) = rb2;
-    *reinterpret_cast<uint4*>(&sB[0][lr + 96][kc]) = rb3;
-    __syncthreads();
+    auto boff = [&](int kt) -> long long {
+        const int k = kt * BK;
+        const int seg = k / p.Kseg;
+        return (long long)seg * p.sB_seg + (k - seg * p.Kseg);
+    };
     const int br0 = MODE == GM_UP_SWIGLU ? wn * 32 : wn * 64;
     const int br1 = MODE == GM_UP_SWIGLU ? 64 + wn * 32 : wn * 64 + 32;
-    for (int kt = 0; kt < nk; ++kt) {
-        const int buf = kt & 1;
-        // prefetch the next k-tile (the last iteration re-reads the current one: no branch,
-        // so the staging registers stay registers)
-        const int kn = kt + 1 < nk ? kt + 1 : kt;
-        {
-            const int k = kn * BK;
-            const long long bo = MOE_BOFF(kn);
-            ra0 = *reinterpret_cast<const uint4*>(ag[0] + k);
-            ra1 = *reinterpret_cast<const uint4*>(ag[1] + k);
-            ra2 = *reinterpret_cast<const uint4*>(ag[2] + k);
-            ra3 = *reinterpret_cast<const uint4*>(ag[3] + k);
-            rb0 = *reinterpret_cast<const uint4*>(bg[0] + bo);
-            rb1 = *reinterpret_cast<const uint4*>(bg[1] + bo);
-            rb2 = *reinterpret_cast<const uint4*>(bg[2] + bo);
-            rb3 = *reinterpret_cast<const uint4*>(bg[3] + bo);
-        }
-#pragma unroll
-        for (int s = 0; s < BK / 16; ++s) {
-            const int ko = s * 16 + (lane >> 5) * 8;
-            const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(&sA[buf][wm * 64 + (lane & 31)][ko]);
-            const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(&sA[buf][wm * 64 + 32 + (lane & 31)][ko]);
-            const bf16x8 b0 = *reinterpret_cast<const bf16x8*>(&sB[buf][br0 + (lane & 31)][ko]);
-            const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(&sB[buf][br1 + (lane & 31)][ko]);
-            acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, acc[0][0], 0, 0, 0);
-            acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b1, acc[0][1], 0, 0, 0);
-            acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b0, acc[1][0], 0, 0, 0);
-            acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, acc[1][1], 0, 0, 0);
-        }
-        const int nb = buf ^ 1;
-        *reinterpret_cast<uint4*>(&sA[nb][lr][kc]) = ra0;
-        *reinterpret_cast<uint4*>(&sA[nb][lr + 32][kc]) = ra1;
-        *reinterpret_cast<uint4*>(&sA[nb][lr + 64][kc]) = ra2;
-        *reinterpret_cast<uint4*>(&sA[nb][lr + 96][kc]) = ra3;
-        *reinterpret_cast<uint4*>(&sB[nb][lr][kc]) = rb0;
-        *reinterpret_cast<uint4*>(&sB[nb][lr + 32][kc]) = rb1;
-        *reinterpret_cast<uint4*>(&sB[nb][lr + 64][kc]) = rb2;
-        *reinterpret_cast<uint4*>(&sB[nb][lr + 96][kc]) = rb3;
-        __syncthreads();
-    }
-#undef MOE_BOFF
+    const int arow = wm * 64;
 
-    // epilogue.  D[i][j] of a 32x32 block: column j = lane % 32,
-    // row i = 8 * (q / 4) + 4 * (lane / 32) + (q % 4) for accumulator element q.
-    if (MODE == GM_DOWN || MODE == GM_DOWN_COMBINE) {
-        // Stage the fp32 tile through LDS, then let 16 threads cover each row with 16-byte
-        // vectors (coalesced stores; the combine reads whole 16-byte pieces of routed rows).
-        float* st = reinterpret_cast<float*>(smem);
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-#pragma unroll
-                for (int q = 0; q < 16; ++q) {
-                    const int rl = wm * 64 + i * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
-                    st[rl * EPW + wn * 64 + j * 32 + (lane & 31)] = acc[i][j][q];
-                }
-        __syncthreads();
-        const int cq = (tid & 15) * 8;
-        const int col0 = ti.nt * BN + cq;
-        if (col0 >= p.N) return;
-        uint16_t* C = (uint16_t*)p.C;
-#pragma unroll 1
-        for (int pr = 0; pr < BM / 16; ++pr) {
-            const int rl = (tid >> 4) + 16 * pr;
-            if (rl >= ti.rows) break;
-            const float4 v0 = *reinterpret_cast<const float4*>(&st[rl * EPW + cq]);
-            const float4 v1 = *reinterpret_cast<const float4*>(&st[rl * EPW + cq + 4]);
-            float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-            const long long row = ti.row0 + rl;
-            if (MODE == GM_DOWN_COMBINE) {
-                // fixed order: residual, shared experts, then k = 0 .. K_r-1
-                if (p.resid) {
-                    const uint4 q = *reinterpret_cast<const uint4*>((const uint16_t*)p.resid + row * p.N + col0);
-                    const uint32_t wv[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        v[2 * e] = __uint_as_float(wv[e] << 16) + v[2 * e];
-                        v[2 * e + 1] = __uint_as_float(wv[e] & 0xFFFF0000u) + v[2 * e + 1];
-                    }
-                }
-                for (int k = 0; k < p.K_r; ++k) {
-                    long long pr_row = (long long)(uint32_t)p.pair_row[row * p.K_r + k];
-                    pr_row = pr_row < p.R ? pr_row : p.R - 1;
-                    const float g = p.topk_w[row * p.K_r + k];
-                    const uint4 q = *reinterpret_cast<const uint4*>((const uint16_t*)p.y_perm + pr_row * p.N + col0);
-                    const uint32_t wv[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        v[2 * e] = fmaf(g, __uint_as_float(wv[e] << 16), v[2 * e]);
-                        v[2 * e + 1] = fmaf(g, __uint_as_float(wv[e] & 0xFFFF0000u), v[2 * e + 1]);
-                    }
-                }
-            }
-            uint4 o;
-            o.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-            o.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
-            o.z = (uint32_t)f32_to_bf16(v[4]) | ((uint32_t)f32_to_bf16(v[5]) << 16);
-            o.w = (uint32_t)f32_to_bf16(v[6]) | ((uint32_t)f32_to_bf16(v[7]) << 16);
-            *reinterpret_cast<uint4*>(C + row * p.ldc + col0) = o;
+    MOE_STAGE_DECL(s0_);
+    MOE_STAGE_DECL(s1_);
+    MOE_STAGE_LOAD(s0_, 0, boff(0));
+    const int k1 = nk > 1 ? 1 : 0;
+    MOE_STAGE_LOAD(s1_, k1 * BK, boff(k1));
+    __syncthreads();  // the previous tile's epilogue may still read the staging area
+    MOE_STAGE_STORE(s0_, 0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; kt += 2) {
+        // even step: compute buffer 0, refill s0 with kt+2, publish s1 (kt+1) into buffer 1
+        {
+            const int kn = kt + 2 < nk ? kt + 2 : nk - 1;
+            MOE_STAGE_LOAD(s0_, kn * BK, boff(kn));
+            mma_tile(c00, c01, c10, c11, sA[0], sB[0], arow, br0, br1, lane);
+            if (kt + 1 < nk) MOE_STAGE_STORE(s1_, 1);
+            __syncthreads();
         }
-        return;
+        if (kt + 1 < nk) {
+            const int kn = kt + 3 < nk ? kt + 3 : nk - 1;
+            MOE_STAGE_LOAD(s1_, kn * BK, boff(kn));
+            mma_tile(c00, c01, c10, c11, sA[1], sB[1], arow, br0, br1, lane);
+            if (kt + 2 < nk) MOE_STAGE_STORE(s0_, 0);
+            __syncthreads();
+        }
     }
+
+    // ---- epilogue: stage through LDS, then each row is covered by 16-byte vectors.
+    // D[i][j] of a 32x32 block: column j = lane % 32, row i = 8 (q / 4) + 4 (lane / 32) + (q % 4).
+    constexpr int OUTW = MODE == GM_UP_SWIGLU ? 64 : BN;  // output columns of the tile
+    float* st = reinterpret_cast<float*>(smem);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+        const int rl = wm * 64 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+        if (MODE == GM_UP_SWIGLU) {
+            st[rl * EPW + wn * 32 + (lane & 31)] = silu(c00[q]) * c01[q];
+            st[(rl + 32) * EPW + wn * 32 + (lane & 31)] = silu(c10[q]) * c11[q];
+        } else {
+            st[rl * EPW + wn * 64 + (lane & 31)] = c00[q];
+            st[rl * EPW + wn * 64 + 32 + (lane & 31)] = c01[q];
+            st[(rl + 32) * EPW + wn * 64 + (lane & 31)] = c10[q];
+            st[(rl + 32) * EPW + wn * 64 + 32 + (lane & 31)] = c11[q];
+        }
+    }
+    __syncthreads();
+    constexpr int TPR = OUTW / 8;    // threads per row
+    constexpr int RPP = 256 / TPR;   // rows per pass
+    const int cq = (tid % TPR) * 8;
+    const int col0 = ti.nt * OUTW + cq;
+    if (col0 >= p.N) return;
     uint16_t* C = (uint16_t*)p.C;
     const long long coff = p.offsets ? 0 : (long long)ti.g * p.sC_group;
+    float bias8[8];
+    if (MODE == GM_UP_RELU) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+        for (int e = 0; e < 8; ++e) bias8[e] = p.bias ? p.bias[(long long)ti.g * p.sbias_group + col0 + e] : 0.f;
+    }
+    for (int rl = tid / TPR; rl < ti.rows; rl += RPP) {
+        const float4 v0 = *reinterpret_cast<const float4*>(&st[rl * EPW + cq]);
+        const float4 v1 = *reinterpret_cast<const float4*>(&st[rl * EPW + cq + 4]);
+        float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+        const long long row = ti.row0 + rl;
+        if (MODE == GM_UP_RELU) {
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-            const int rl = wm * 64 + i * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
-            if (rl >= ti.rows) continue;
-            uint16_t* crow = C + (long long)(ti.row0 + rl) * p.ldc + coff;
-            if (MODE == GM_UP_SWIGLU) {
-                const int col = ti.nt * 64 + wn * 32 + (lane & 31);
-                crow[col] = f32_to_bf16(silu(acc[i][0][q]) * acc[i][1][q]);
-            } else {
+            for (int e = 0; e < 8; ++e) v[e] = fmaxf(v[e] + bias8[e], 0.0f);
+        }
+        if (MODE == GM_DOWN_COMBINE) {
+            // fixed order: residual + shared experts, then the routed rows k = 0 .. K_r-1
+            if (p.resid) {
+                const uint4 q = *reinterpret_cast<const uint4*>((const uint16_t*)p.resid + row * p.N + col0);
+                float u8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+                add8_bf16(u8, q);
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const int col = ti.nt * BN + wn * 64 + j * 32 + (lane & 31);
-                    if (col >= p.N) continue;
-                    float v = acc[i][j][q];
-                    if (MODE == GM_UP_RELU) {
-                        if (p.bias) v += p.bias[(long long)ti.g * p.sbias_group + col];
-                        v = fmaxf(v, 0.0f);
-                    }
-                    crow[col] = f32_to_bf16(v);
+                for (int e = 0; e < 8; ++e) v[e] = u8[e] + v[e];
+            }
+            const int32_t* prr = p.pair_row + row * p.K_r;
+            const float* gr = p.topk_w + row * p.K_r;
+            int k = 0;
+            for (; k + 4 <= p.K_r; k += 4) {
+                long long r4[4];
+                float g4[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const long long x = (long long)(uint32_t)prr[k + e];
+                    r4[e] = x < p.R ? x : p.R - 1;
+                    g4[e] = gr[k + e];
                 }
+                uint4 y4[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    y4[e] = *reinterpret_cast<const uint4*>((const uint16_t*)p.y_perm + r4[e] * p.N + col0);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) fma8_bf16(v, g4[e], y4[e]);
+            }
+            for (; k < p.K_r; ++k) {
+                long long x = (long long)(uint32_t)prr[k];
+                x = x < p.R ? x : p.R - 1;
+                fma8_bf16(v, gr[k], *reinterpret_cast<const uint4*>((const uint16_t*)p.y_perm + x * p.N + col0));
             }
         }
+        *reinterpret_cast<uint4*>(C + row * p.ldc + coff + col0) = pack8_bf16(v);
+    }
+}
+
+__device__ __forceinline__ int total_tiles(const GemmParams& p, int NT) {
+    if (p.offsets) return p.tiles[p.G] * NT;
+    return p.G * ((p.M_dense + BM - 1) / BM) * NT;
+}
+
+template <int MODE>
+__global__ __launch_bounds__(256, 2) void k_gemm_bf16(GemmParams p, int NT) {
+    __shared__ __attribute__((aligned(16))) unsigned char smem[kSmemBytes];
+    const int total = total_tiles(p, NT);
+    const int xcd = blockIdx.x & 7, loc = blockIdx.x >> 3, per_xcd = gridDim.x >> 3;
+    const int beg = (int)((long long)total * xcd / 8);
+    const int end = (int)((long long)total * (xcd + 1) / 8);
+    for (int L = beg + loc; L < end; L += per_xcd) {
+        TileInfo ti;
+        decode_tile(p, NT, BM, L, ti);
+        gemm_tile<MODE>(p, ti, smem);
     }
 }
 
@@ -371,12 +431,14 @@ hipError_t launch_gemm(int dtype, int mode, const GemmParams& p, hipStream_t s) 
     }
     const int NT = mode == GM_UP_SWIGLU ? (p.N + 63) / 64 : (p.N + BN - 1) / BN;
     if (mode == GM_DOWN_COMBINE && p.offsets) return hipErrorInvalidValue;  // dense (shared) groups only
+    // persistent grid: two workgroups per CU (LDS and registers allow two), a multiple of 8
     long long mt;
-    if (p.offsets) mt = (p.max_rows + BM - 1) / BM + p.G;  // sum of ceil(rows_g / BM) <= this
+    if (p.offsets) mt = (p.max_rows + BM - 1) / BM + p.G;  // upper bound of sum ceil(rows_g / BM)
     else mt = (long long)p.G * ((p.M_dense + BM - 1) / BM);
-    long long nb = mt * NT;
+    long long nb = 2LL * device_cus();
+    const long long need = (mt * NT + 7) / 8 * 8;
+    nb = nb < need ? nb : need;
     nb = (nb + 7) / 8 * 8;
-    if (nb > 0x7FFFFFF8LL) return hipErrorInvalidValue;
     if (mode == GM_UP_SWIGLU) hipLaunchKernelGGL(k_gemm_bf16<GM_UP_SWIGLU>, dim3((unsigned)nb), dim3(256), 0, s, p, NT);
     else if (mode == GM_UP_RELU) hipLaunchKernelGGL(k_gemm_bf16<GM_UP_RELU>, dim3((unsigned)nb), dim3(256), 0, s, p, NT);
     else if (mode == GM_DOWN) hipLaunchKernelGGL(k_gemm_bf16<GM_DOWN>, dim3((unsigned)nb), dim3(256), 0, s, p, NT);

@@ -75,3 +75,21 @@ def test_calls_rejected_before_any_launch():
                                  None, None, None, 0, None) == moe.MOE_OK
     assert lib.moe_profile_query(99, ctypes.byref(ctypes.c_int64()), ctypes.byref(ctypes.c_double())) == \
         moe.MOE_ERR_INVALID_ARG
+
+
+def test_no_kernel_uses_scratch_memory():
+    """Every HIP kernel keeps its working set in registers/LDS (hipcc resource report)."""
+    import subprocess
+    from fine_grained_shared_amd import build as hb
+    for src in hb.SOURCES:
+        out = subprocess.run([os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")] + hb.FLAGS +
+                             ["-c", os.path.join(hb.CSRC, src), "-o", os.devnull,
+                              "-Rpass-analysis=kernel-resource-usage"],
+                             capture_output=True, text=True)
+        assert out.returncode == 0, out.stderr[-2000:]
+        names = re.findall(r"Function Name: (\S+)", out.stderr)
+        scratch = [int(x) for x in re.findall(r"ScratchSize \[bytes/lane\]: (\d+)", out.stderr)]
+        assert len(names) == len(scratch)
+        assert names or src == "api.hip"   # the C-ABI file holds host code only
+        bad = [n for n, sz in zip(names, scratch) if sz]
+        assert not bad, "kernels using scratch: %s" % bad
