@@ -10,15 +10,27 @@
 // operands staged through double-buffered LDS.  For SwiGLU the 128 weight rows of a tile are
 // 64 gate rows and the 64 matching up rows, so the epilogue has both halves of every output
 // element in the same lane.  fp32 path: plain VALU kernels (the tiny fp32 layer only).
+#include <stdlib.h>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace moe {
 
 constexpr int BM = 128, BN = 128, BK = 64;
-constexpr int LDSW = BK + 8;  // padded LDS row (elements)
 
 int gemm_bm(int dtype) { return dtype == 0 ? 1 : BM; }
+
+// The wide-tile kernel can be switched off with MOE_GEMM_WIDE=0 (for A/B measurements).
+static bool wide_ok() {
+    static int v = -1;
+    if (v < 0) {
+        const char* e = getenv("MOE_GEMM_WIDE");
+        v = (e && e[0] == '0') ? 0 : 1;
+    }
+    return v == 1;
+}
+
 
 // Compute units of the current device (cached per device id).
 static int device_cus() {
@@ -75,11 +87,25 @@ struct TileInfo {
     int g, row0, rows, nt;
 };
 
+// Inside a group of nm m-tiles x NT n-tiles the tiles are visited in blocks of kGroupM m-tiles
+// (m fastest, then n), so that a window of concurrently running tiles covers a few m-tiles
+// times a few n-tiles and reuses both operands from L2 instead of streaming one of them.
+constexpr int kGroupM = 8;
+
+__device__ __forceinline__ void blocked_mn(int Lg, int nm, int NT, int& ml, int& nt) {
+    const int blk = Lg / (kGroupM * NT);
+    const int m0 = blk * kGroupM;
+    const int bm = min(kGroupM, nm - m0);
+    const int r = Lg - blk * kGroupM * NT;
+    nt = r / bm;
+    ml = m0 + (r - nt * bm);
+}
+
 __device__ __forceinline__ bool decode_tile(const GemmParams& p, int NT, int bm, int L, TileInfo& ti) {
     if (p.offsets) {
         const int total = p.tiles[p.G];
         if (L >= total * NT) return false;
-        const int mt = L / NT;  // only for the binary search: tiles[g] * NT <= L  <=>  tiles[g] <= L / NT
+        const int mt = L / NT;  // tiles[g] * NT <= L  <=>  tiles[g] <= L / NT
         int lo = 0, hi = p.G;
         while (hi - lo > 1) {
             const int mid = (lo + hi) >> 1;
@@ -88,10 +114,9 @@ __device__ __forceinline__ bool decode_tile(const GemmParams& p, int NT, int bm,
         }
         const int g = lo;
         const int t0 = p.tiles[g], nm = p.tiles[g + 1] - t0;
-        const int Lg = L - t0 * NT;
+        int ml;
+        blocked_mn(L - t0 * NT, nm, NT, ml, ti.nt);
         ti.g = g;
-        ti.nt = Lg / nm;
-        const int ml = Lg - ti.nt * nm;
         ti.row0 = p.offsets[g] + ml * bm;
         ti.rows = min(bm, p.offsets[g + 1] - ti.row0);
     } else {
@@ -99,9 +124,8 @@ __device__ __forceinline__ bool decode_tile(const GemmParams& p, int NT, int bm,
         const int per = nm * NT;
         if (L >= p.G * per) return false;
         ti.g = L / per;
-        const int Lg = L - ti.g * per;
-        ti.nt = Lg / nm;
-        const int ml = Lg - ti.nt * nm;
+        int ml;
+        blocked_mn(L - ti.g * per, nm, NT, ml, ti.nt);
         ti.row0 = ml * bm;
         ti.rows = min(bm, p.M_dense - ti.row0);
     }
@@ -112,49 +136,39 @@ __device__ __forceinline__ bool decode_tile(const GemmParams& p, int NT, int bm,
 // Persistent: the grid holds two workgroups per CU; the workgroups of one XCD walk a
 // contiguous range of the tile list (so concurrently running tiles of an XCD share weight
 // and activation tiles in its L2), strided by the number of workgroups on that XCD.
-// Pipeline: k-tile kt+2 is fetched into registers while k-tile kt is multiplied out of LDS
-// and k-tile kt+1 waits in the other register set, so each global load has two iterations
-// to arrive.  Epilogues stage the fp32 tile through LDS and store 16-byte vectors.
-constexpr int EPW = BN + 4;  // fp32 staging row (floats)
-constexpr int kSmemBytes = 2 * (BM + BN) * LDSW * 2;
-static_assert(BM * EPW * 4 <= kSmemBytes, "epilogue staging must fit in the operand buffers");
+//
+// Operand tiles (128 rows x 64 k, bf16) move global -> LDS with global_load_lds_dwordx4: one
+// instruction moves 64 lanes x 16 bytes into 1 KB of LDS (lane i -> bytes [16 i, 16 i + 16)),
+// so there is no register staging.  LDS rows are 128 bytes, unpadded; the 16-byte chunk c of
+// row r is stored in slot c ^ ((r >> 1) & 7).  Two rows share one 256-byte window of the 64
+// banks, so this spreads the fragment reads of 16 consecutive rows at one k offset over all
+// 64 banks.  The compiler does not track these LDS writes, so every hand-off
+// is an explicit vmcnt(0) wait plus a workgroup barrier.  Epilogues stage the fp32 tile
+// through LDS and store 16-byte vectors.
+constexpr int EPW = BN + 4;                               // fp32 staging row (floats)
+constexpr int kTileBytes = BM * BK * 2;                   // one operand tile (16 KB)
+constexpr int kStageBytes = 2 * kTileBytes;               // A + B
+constexpr int kSmemBytes = BM * EPW * 4 > 2 * kStageBytes ? BM * EPW * 4 : 2 * kStageBytes;
+static_assert(BM == BN && BM == 128 && BK == 64, "tile layout assumes 128 x 128 x 64");
 
-// Global -> register staging of one k-tile (4 A rows and 4 weight rows of 16 bytes per
-// thread), and register -> LDS.  Macros over named registers keep the staging in VGPRs.
-#define MOE_STAGE_DECL(S) uint4 S##a0, S##a1, S##a2, S##a3, S##b0, S##b1, S##b2, S##b3
-#define MOE_STAGE_LOAD(S, k, bo)                                   \
-    do {                                                           \
-        S##a0 = *reinterpret_cast<const uint4*>(ag0 + (k));        \
-        S##a1 = *reinterpret_cast<const uint4*>(ag1 + (k));        \
-        S##a2 = *reinterpret_cast<const uint4*>(ag2 + (k));        \
-        S##a3 = *reinterpret_cast<const uint4*>(ag3 + (k));        \
-        S##b0 = *reinterpret_cast<const uint4*>(bg0 + (bo));       \
-        S##b1 = *reinterpret_cast<const uint4*>(bg1 + (bo));       \
-        S##b2 = *reinterpret_cast<const uint4*>(bg2 + (bo));       \
-        S##b3 = *reinterpret_cast<const uint4*>(bg3 + (bo));       \
-    } while (0)
-#define MOE_STAGE_STORE(S, buf)                                            \
-    do {                                                                   \
-        *reinterpret_cast<uint4*>(&sA[buf][lr][kc]) = S##a0;              \
-        *reinterpret_cast<uint4*>(&sA[buf][lr + 32][kc]) = S##a1;         \
-        *reinterpret_cast<uint4*>(&sA[buf][lr + 64][kc]) = S##a2;         \
-        *reinterpret_cast<uint4*>(&sA[buf][lr + 96][kc]) = S##a3;         \
-        *reinterpret_cast<uint4*>(&sB[buf][lr][kc]) = S##b0;              \
-        *reinterpret_cast<uint4*>(&sB[buf][lr + 32][kc]) = S##b1;         \
-        *reinterpret_cast<uint4*>(&sB[buf][lr + 64][kc]) = S##b2;         \
-        *reinterpret_cast<uint4*>(&sB[buf][lr + 96][kc]) = S##b3;         \
-    } while (0)
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+__device__ __forceinline__ void dma16(const void* g, unsigned char* lds_chunk) {
+    __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)lds_chunk, 16, 0, 0);
+}
 
 __device__ __forceinline__ void mma_tile(f32x16& c00, f32x16& c01, f32x16& c10, f32x16& c11,
-                                         const uint16_t (*sa)[LDSW], const uint16_t (*sb)[LDSW], int arow, int br0,
+                                         const unsigned char* sa, const unsigned char* sb, int arow, int br0,
                                          int br1, int lane) {
+    const int rA0 = arow + (lane & 31), rA1 = rA0 + 32;
+    const int rB0 = br0 + (lane & 31), rB1 = br1 + (lane & 31);
 #pragma unroll
     for (int s = 0; s < BK / 16; ++s) {
-        const int ko = s * 16 + (lane >> 5) * 8;
-        const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(&sa[arow + (lane & 31)][ko]);
-        const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(&sa[arow + 32 + (lane & 31)][ko]);
-        const bf16x8 b0 = *reinterpret_cast<const bf16x8*>(&sb[br0 + (lane & 31)][ko]);
-        const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(&sb[br1 + (lane & 31)][ko]);
+        const int kc = 2 * s + (lane >> 5);   // logical 16-byte chunk of the 64-wide k-tile
+        const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(sa + rA0 * 128 + ((kc ^ ((rA0 >> 1) & 7)) << 4));
+        const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(sa + rA1 * 128 + ((kc ^ ((rA1 >> 1) & 7)) << 4));
+        const bf16x8 b0 = *reinterpret_cast<const bf16x8*>(sb + rB0 * 128 + ((kc ^ ((rB0 >> 1) & 7)) << 4));
+        const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(sb + rB1 * 128 + ((kc ^ ((rB1 >> 1) & 7)) << 4));
         c00 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, c00, 0, 0, 0);
         c01 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b1, c01, 0, 0, 0);
         c10 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b0, c10, 0, 0, 0);
@@ -189,37 +203,107 @@ __device__ __forceinline__ void fma8_bf16(float (&v)[8], float g, uint4 q) {
     }
 }
 
+// Epilogue of one 8-column piece of output row rl (tile-local) starting at column col0:
+// bias + ReLU (ReLU up), residual + gate-weighted routed rows (shared down + combine),
+// then one bf16 rounding and a 16-byte store.
+template <int MODE>
+__device__ __forceinline__ void epilogue_row(const GemmParams& p, const TileInfo& ti, float (&v)[8], int rl,
+                                             int col0) {
+    const long long row = ti.row0 + rl;
+    if (MODE == GM_UP_RELU) {
+        if (p.bias) {
+            const float* bb = p.bias + (long long)ti.g * p.sbias_group + col0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] += bb[e];
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = fmaxf(v[e], 0.0f);
+    }
+    if (MODE == GM_DOWN_COMBINE) {
+        // fixed order: residual + shared experts, then the routed rows k = 0 .. K_r-1
+        if (p.resid) {
+            const uint4 q = *reinterpret_cast<const uint4*>((const uint16_t*)p.resid + row * p.N + col0);
+            float u8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            add8_bf16(u8, q);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = u8[e] + v[e];
+        }
+        const int32_t* prr = p.pair_row + row * p.K_r;
+        const float* gr = p.topk_w + row * p.K_r;
+        int k = 0;
+        for (; k + 4 <= p.K_r; k += 4) {
+            long long r4[4];
+            float g4[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const long long x = (long long)(uint32_t)prr[k + e];
+                r4[e] = x < p.R ? x : p.R - 1;
+                g4[e] = gr[k + e];
+            }
+            uint4 y4[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                y4[e] = *reinterpret_cast<const uint4*>((const uint16_t*)p.y_perm + r4[e] * p.N + col0);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) fma8_bf16(v, g4[e], y4[e]);
+        }
+        for (; k < p.K_r; ++k) {
+            long long x = (long long)(uint32_t)prr[k];
+            x = x < p.R ? x : p.R - 1;
+            fma8_bf16(v, gr[k], *reinterpret_cast<const uint4*>((const uint16_t*)p.y_perm + x * p.N + col0));
+        }
+    }
+    const long long coff = p.offsets ? 0 : (long long)ti.g * p.sC_group;
+    if (MODE == GM_F32OUT) {
+        float* C = (float*)p.C + row * p.ldc + coff + col0;
+        reinterpret_cast<float4*>(C)[0] = make_float4(v[0], v[1], v[2], v[3]);
+        reinterpret_cast<float4*>(C)[1] = make_float4(v[4], v[5], v[6], v[7]);
+        return;
+    }
+    uint16_t* C = (uint16_t*)p.C;
+    *reinterpret_cast<uint4*>(C + row * p.ldc + coff + col0) = pack8_bf16(v);
+}
+
 template <int MODE>
 __device__ __forceinline__ void gemm_tile(const GemmParams& p, const TileInfo& ti, unsigned char* smem) {
-    auto sA = reinterpret_cast<uint16_t(*)[BM][LDSW]>(smem);
-    auto sB = reinterpret_cast<uint16_t(*)[BN][LDSW]>(smem + 2 * BM * LDSW * 2);
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
-    const int lr = tid >> 3;       // 0..31: row handled by this thread in each 32-row slab
-    const int kc = (tid & 7) * 8;  // element offset of this thread's 16-byte chunk
 
+    // DMA assignment: wave w moves 1 KB chunks c = 4 w + i (i < 4) of each operand tile; chunk c
+    // is rows 8c .. 8c+7; lane l of it is row 8c + l/8, LDS slot l%8, global chunk (l%8) ^ ((row>>1)&7).
     const uint16_t* A = (const uint16_t*)p.A;
     const uint16_t* Bg = (const uint16_t*)p.B + (size_t)ti.g * p.sB_group;
     const uint16_t* ag[4];
     const uint16_t* bg[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int r = min(lr + 32 * i, ti.rows - 1);
+        const int row = 8 * (4 * w + i) + (lane >> 3);
+        const int kcg = ((lane & 7) ^ ((row >> 1) & 7)) * 8;   // element offset of the global chunk
+        const int r = min(row, ti.rows - 1);
         long long src = ti.row0 + r;
         if (p.a_rows) src = min(max((long long)p.a_rows[src], 0LL), p.a_nrows - 1);
-        ag[i] = A + src * p.lda + kc;
-        const int rb = lr + 32 * i;
+        ag[i] = A + src * p.lda + kcg;
         int wr;
         if (MODE == GM_UP_SWIGLU) {
             const int n0 = ti.nt * 64;
-            wr = rb < 64 ? n0 + rb : p.up_off + n0 + (rb - 64);
+            wr = row < 64 ? n0 + row : p.up_off + n0 + (row - 64);
         } else {
-            wr = min(ti.nt * BN + rb, p.N - 1);
+            wr = min(ti.nt * BN + row, p.N - 1);
         }
-        bg[i] = Bg + (size_t)wr * p.ldb + kc;
+        bg[i] = Bg + (size_t)wr * p.ldb + kcg;
     }
-    const uint16_t *ag0 = ag[0], *ag1 = ag[1], *ag2 = ag[2], *ag3 = ag[3];
-    const uint16_t *bg0 = bg[0], *bg1 = bg[1], *bg2 = bg[2], *bg3 = bg[3];
+    auto issue = [&](int kt, int buf) {
+        const int k = kt * BK;
+        const int seg = k / p.Kseg;
+        const long long bo = (long long)seg * p.sB_seg + (k - seg * p.Kseg);
+        unsigned char* sa = smem + buf * kStageBytes;
+        unsigned char* sb = sa + kTileBytes;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            dma16(ag[i] + k, sa + (4 * w + i) * 1024);
+            dma16(bg[i] + bo, sb + (4 * w + i) * 1024);
+        }
+    };
 
     f32x16 c00, c01, c10, c11;
 #pragma unroll
@@ -229,41 +313,22 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const TileInfo& t
         c10[q] = 0.f;
         c11[q] = 0.f;
     }
-
-    const int nk = p.K / BK;
-    auto boff = [&](int kt) -> long long {
-        const int k = kt * BK;
-        const int seg = k / p.Kseg;
-        return (long long)seg * p.sB_seg + (k - seg * p.Kseg);
-    };
     const int br0 = MODE == GM_UP_SWIGLU ? wn * 32 : wn * 64;
     const int br1 = MODE == GM_UP_SWIGLU ? 64 + wn * 32 : wn * 64 + 32;
     const int arow = wm * 64;
+    const int nk = p.K / BK;
 
-    MOE_STAGE_DECL(s0_);
-    MOE_STAGE_DECL(s1_);
-    MOE_STAGE_LOAD(s0_, 0, boff(0));
-    const int k1 = nk > 1 ? 1 : 0;
-    MOE_STAGE_LOAD(s1_, k1 * BK, boff(k1));
-    __syncthreads();  // the previous tile's epilogue may still read the staging area
-    MOE_STAGE_STORE(s0_, 0);
+    __syncthreads();  // the previous tile's epilogue may still read the LDS staging area
+    issue(0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    for (int kt = 0; kt < nk; kt += 2) {
-        // even step: compute buffer 0, refill s0 with kt+2, publish s1 (kt+1) into buffer 1
-        {
-            const int kn = kt + 2 < nk ? kt + 2 : nk - 1;
-            MOE_STAGE_LOAD(s0_, kn * BK, boff(kn));
-            mma_tile(c00, c01, c10, c11, sA[0], sB[0], arow, br0, br1, lane);
-            if (kt + 1 < nk) MOE_STAGE_STORE(s1_, 1);
-            __syncthreads();
-        }
-        if (kt + 1 < nk) {
-            const int kn = kt + 3 < nk ? kt + 3 : nk - 1;
-            MOE_STAGE_LOAD(s1_, kn * BK, boff(kn));
-            mma_tile(c00, c01, c10, c11, sA[1], sB[1], arow, br0, br1, lane);
-            if (kt + 2 < nk) MOE_STAGE_STORE(s0_, 0);
-            __syncthreads();
-        }
+    for (int kt = 0; kt < nk; ++kt) {
+        const int buf = kt & 1;
+        if (kt + 1 < nk) issue(kt + 1, buf ^ 1);   // that buffer was last read before the previous barrier
+        mma_tile(c00, c01, c10, c11, smem + buf * kStageBytes, smem + buf * kStageBytes + kTileBytes, arow, br0,
+                 br1, lane);
+        __builtin_amdgcn_s_waitcnt(0);               // the next tile has landed in LDS
+        __syncthreads();
     }
 
     // ---- epilogue: stage through LDS, then each row is covered by 16-byte vectors.
@@ -289,57 +354,11 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const TileInfo& t
     const int cq = (tid % TPR) * 8;
     const int col0 = ti.nt * OUTW + cq;
     if (col0 >= p.N) return;
-    uint16_t* C = (uint16_t*)p.C;
-    const long long coff = p.offsets ? 0 : (long long)ti.g * p.sC_group;
-    float bias8[8];
-    if (MODE == GM_UP_RELU) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) bias8[e] = p.bias ? p.bias[(long long)ti.g * p.sbias_group + col0 + e] : 0.f;
-    }
     for (int rl = tid / TPR; rl < ti.rows; rl += RPP) {
         const float4 v0 = *reinterpret_cast<const float4*>(&st[rl * EPW + cq]);
         const float4 v1 = *reinterpret_cast<const float4*>(&st[rl * EPW + cq + 4]);
         float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-        const long long row = ti.row0 + rl;
-        if (MODE == GM_UP_RELU) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = fmaxf(v[e] + bias8[e], 0.0f);
-        }
-        if (MODE == GM_DOWN_COMBINE) {
-            // fixed order: residual + shared experts, then the routed rows k = 0 .. K_r-1
-            if (p.resid) {
-                const uint4 q = *reinterpret_cast<const uint4*>((const uint16_t*)p.resid + row * p.N + col0);
-                float u8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-                add8_bf16(u8, q);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) v[e] = u8[e] + v[e];
-            }
-            const int32_t* prr = p.pair_row + row * p.K_r;
-            const float* gr = p.topk_w + row * p.K_r;
-            int k = 0;
-            for (; k + 4 <= p.K_r; k += 4) {
-                long long r4[4];
-                float g4[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const long long x = (long long)(uint32_t)prr[k + e];
-                    r4[e] = x < p.R ? x : p.R - 1;
-                    g4[e] = gr[k + e];
-                }
-                uint4 y4[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    y4[e] = *reinterpret_cast<const uint4*>((const uint16_t*)p.y_perm + r4[e] * p.N + col0);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) fma8_bf16(v, g4[e], y4[e]);
-            }
-            for (; k < p.K_r; ++k) {
-                long long x = (long long)(uint32_t)prr[k];
-                x = x < p.R ? x : p.R - 1;
-                fma8_bf16(v, gr[k], *reinterpret_cast<const uint4*>((const uint16_t*)p.y_perm + x * p.N + col0));
-            }
-        }
-        *reinterpret_cast<uint4*>(C + row * p.ldc + coff + col0) = pack8_bf16(v);
+        epilogue_row<MODE>(p, ti, v, rl, col0);
     }
 }
 
@@ -360,6 +379,194 @@ __global__ __launch_bounds__(256, 2) void k_gemm_bf16(GemmParams p, int NT) {
         decode_tile(p, NT, BM, L, ti);
         gemm_tile<MODE>(p, ti, smem);
     }
+}
+
+// ---------------------------------------------------------------- bf16 MFMA grouped GEMM, wide tile
+// 128 rows x 512 output columns per workgroup (twice the arithmetic per byte moved of the
+// 128 x 128 tile).  Two 80 KB operand stages fill the LDS; one workgroup per CU.  Same
+// swizzled DMA staging and explicit hand-offs as the 128 x 128 kernel.
+constexpr int WBN = 512;
+constexpr int kWTileA = BM * BK * 2;          // 16 KB
+constexpr int kWTileB = WBN * BK * 2;         // 64 KB
+constexpr int kWStage = kWTileA + kWTileB;    // 80 KB
+constexpr int kWSmem = 2 * kWStage;           // 160 KB
+constexpr int WEPW_SW = 256 + 4;              // SwiGLU staging row: 256 outputs
+constexpr int WEPW = WBN + 4;                 // other modes: 512 outputs, staged 64 rows at a time
+static_assert(BM * WEPW_SW * 4 <= kWSmem && 64 * WEPW * 4 <= kWSmem, "wide epilogue staging must fit");
+
+__device__ __forceinline__ const bf16x8& frag(const unsigned char* base, int row, int kc) {
+    return *reinterpret_cast<const bf16x8*>(base + row * 128 + ((kc ^ ((row >> 1) & 7)) << 4));
+}
+
+// Eight waves (two per SIMD), each owning a 128 x 64 block (4 x 2 accumulators).  Issue is in
+// order, and a DMA issue stalls its wave for tens of cycles while the CU's address unit is busy;
+// the other wave of the SIMD keeps the matrix pipe fed meanwhile.
+template <int MODE>
+__device__ __forceinline__ void gemm_tile_wide8(const GemmParams& p, const TileInfo& ti, unsigned char* smem) {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, w = tid >> 6;   // w < 8
+
+    const uint16_t* A = (const uint16_t*)p.A;
+    const uint16_t* Bg = (const uint16_t*)p.B + (size_t)ti.g * p.sB_group;
+    // A: 16 chunks, wave w moves chunks 2w, 2w+1 (rows 16 w + 8 i + lane/8)
+    const uint16_t* ag[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int row = 8 * (2 * w + i) + (lane >> 3);
+        const int kcg = ((lane & 7) ^ ((row >> 1) & 7)) * 8;
+        const int r = min(row, ti.rows - 1);
+        long long src = ti.row0 + r;
+        if (p.a_rows) src = min(max((long long)p.a_rows[src], 0LL), p.a_nrows - 1);
+        ag[i] = A + src * p.lda + kcg;
+    }
+    // B: 64 chunks, wave w moves chunks 8w .. 8w+7 (rows 64 w + 8 i + lane/8)
+    int wrow0, wrow_max;
+    if (MODE == GM_UP_SWIGLU) {
+        const int n0 = ti.nt * 256;
+        const int r0 = 64 * w + (lane >> 3);
+        wrow0 = r0 < 256 ? n0 + r0 : p.up_off + n0 + (r0 - 256);
+        wrow_max = r0 < 256 ? p.N - 1 : p.up_off + p.N - 1;
+    } else {
+        wrow0 = ti.nt * WBN + 64 * w + (lane >> 3);
+        wrow_max = p.N - 1;
+    }
+    auto dma_chunk = [&](int kt, int buf, int c) {   // c < 10: c < 2 -> A, else B chunk c - 2
+        const int k = kt * BK;
+        unsigned char* sa = smem + buf * kWStage;
+        if (c < 2) {
+            dma16(ag[c] + k, sa + (2 * w + c) * 1024);
+        } else {
+            const int i = c - 2;
+            const int seg = k / p.Kseg;
+            const long long bo = (long long)seg * p.sB_seg + (k - seg * p.Kseg);
+            const int wr = min(wrow0 + 8 * i, wrow_max);
+            const int kcg = ((lane & 7) ^ ((4 * i + (lane >> 4)) & 7)) * 8;   // row = 64 w + 8 i + lane/8
+            dma16(Bg + (size_t)wr * p.ldb + kcg + bo, sa + kWTileA + (8 * w + i) * 1024);
+        }
+    };
+
+    f32x16 acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+    int brow[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) brow[j] = MODE == GM_UP_SWIGLU ? 256 * j + 32 * w : 64 * w + 32 * j;
+    const int nk = p.K / BK;
+
+    // k-step schedule as in the four-wave kernel: sub-steps 0-1 carry the DMA issues, the
+    // wait + barrier sits before sub-step 3, which prefetches the next tile's fragments.
+    bf16x8 af[2][4], bfr[2][2];
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < 10; ++c) dma_chunk(0, 0, c);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) af[0][i] = frag(smem, 32 * i + (lane & 31), lane >> 5);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) bfr[0][j] = frag(smem + kWTileA, brow[j] + (lane & 31), lane >> 5);
+    for (int kt = 0; kt < nk; ++kt) {
+        const int buf = kt & 1;
+        const int kn = kt + 1 < nk ? kt + 1 : kt;
+        const unsigned char* sa = smem + buf * kWStage;
+        const unsigned char* na = smem + (buf ^ 1) * kWStage;
+#pragma unroll
+        for (int s = 0; s < BK / 16; ++s) {
+            const int cur = s & 1;
+            if (s == 3) {
+                __builtin_amdgcn_sched_barrier(0);
+                __builtin_amdgcn_s_waitcnt(0);
+                __syncthreads();
+            }
+            const unsigned char* fa = s < 3 ? sa : na;
+            const int kc = 2 * ((s + 1) & 3) + (lane >> 5);
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                __builtin_amdgcn_sched_barrier(0);
+                acc[g][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][g], bfr[cur][0], acc[g][0], 0, 0, 0);
+                acc[g][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][g], bfr[cur][1], acc[g][1], 0, 0, 0);
+                af[cur ^ 1][g] = frag(fa, 32 * g + (lane & 31), kc);
+                if (g < 2) bfr[cur ^ 1][g] = frag(fa + kWTileA, brow[g] + (lane & 31), kc);
+                if (s < 2) {
+                    const int c = 5 * s + g;
+                    dma_chunk(kn, buf ^ 1, c);
+                    if (g == 3) dma_chunk(kn, buf ^ 1, c + 1);
+                }
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    __syncthreads();
+
+    // ---- epilogue
+    float* st = reinterpret_cast<float*>(smem);
+    if (MODE == GM_UP_SWIGLU) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const int rl = 32 * i + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+                st[rl * WEPW_SW + 32 * w + (lane & 31)] = silu(acc[i][0][q]) * acc[i][1][q];
+            }
+        __syncthreads();
+        const int cq = (tid & 31) * 8;
+        const int col0 = ti.nt * 256 + cq;
+        if (col0 < p.N) {
+            for (int rl = tid >> 5; rl < ti.rows; rl += 16) {
+                const float4 v0 = *reinterpret_cast<const float4*>(&st[rl * WEPW_SW + cq]);
+                const float4 v1 = *reinterpret_cast<const float4*>(&st[rl * WEPW_SW + cq + 4]);
+                float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+                epilogue_row<MODE>(p, ti, v, rl, col0);
+            }
+        }
+        return;
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {   // rows [64 h, 64 h + 64)
+        if (h) __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                    const int rl = 32 * i + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+                    st[rl * WEPW + 64 * w + 32 * j + (lane & 31)] = acc[2 * h + i][j][q];
+                }
+        __syncthreads();
+        const int cq = lane * 8;
+        const int col0 = ti.nt * WBN + cq;
+        if (col0 < p.N) {
+            for (int rl = w; rl < 64 && 64 * h + rl < ti.rows; rl += 8) {
+                const float4 v0 = *reinterpret_cast<const float4*>(&st[rl * WEPW + cq]);
+                const float4 v1 = *reinterpret_cast<const float4*>(&st[rl * WEPW + cq + 4]);
+                float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+                epilogue_row<MODE>(p, ti, v, 64 * h + rl, col0);
+            }
+        }
+    }
+}
+
+template <int MODE>
+__global__ __launch_bounds__(512, 1) void k_gemm_bf16_wide8(GemmParams p, int NT) {
+    __shared__ __attribute__((aligned(16))) unsigned char smem[kWSmem];
+    const int total = total_tiles(p, NT);
+    const int xcd = blockIdx.x & 7, loc = blockIdx.x >> 3, per_xcd = gridDim.x >> 3;
+    const int beg = (int)((long long)total * xcd / 8);
+    const int end = (int)((long long)total * (xcd + 1) / 8);
+    for (int L = beg + loc; L < end; L += per_xcd) {
+        TileInfo ti;
+        decode_tile(p, NT, BM, L, ti);
+        gemm_tile_wide8<MODE>(p, ti, smem);
+    }
+}
+
+__device__ __forceinline__ int wide_nt(const GemmParams& p, int mode) {
+    return mode == GM_UP_SWIGLU ? (p.N + 255) / 256 : (p.N + WBN - 1) / WBN;
 }
 
 // ---------------------------------------------------------------- fp32 VALU path
@@ -422,26 +629,44 @@ __global__ __launch_bounds__(256) void k_gemm_f32(GemmParams p) {
 hipError_t launch_gemm(int dtype, int mode, const GemmParams& p, hipStream_t s) {
     if (p.G == 0 || p.max_rows == 0 || p.N == 0) return hipSuccess;
     if (dtype == 0) {
-        if (mode == GM_DOWN_COMBINE) return hipErrorInvalidValue;  // fp32 layers combine separately
+        if (mode == GM_DOWN_COMBINE || mode == GM_F32OUT) return hipErrorInvalidValue;  // bf16 modes only
         dim3 grid((p.N + 63) / 64, (p.max_rows + 3) / 4, p.offsets ? 1 : p.G);
         if (mode == GM_UP_SWIGLU) hipLaunchKernelGGL(k_gemm_f32<GM_UP_SWIGLU>, grid, dim3(256), 0, s, p);
         else if (mode == GM_UP_RELU) hipLaunchKernelGGL(k_gemm_f32<GM_UP_RELU>, grid, dim3(256), 0, s, p);
         else hipLaunchKernelGGL(k_gemm_f32<GM_DOWN>, grid, dim3(256), 0, s, p);
         return hipGetLastError();
     }
-    const int NT = mode == GM_UP_SWIGLU ? (p.N + 63) / 64 : (p.N + BN - 1) / BN;
     if (mode == GM_DOWN_COMBINE && p.offsets) return hipErrorInvalidValue;  // dense (shared) groups only
-    // persistent grid: two workgroups per CU (LDS and registers allow two), a multiple of 8
-    long long mt;
-    if (p.offsets) mt = (p.max_rows + BM - 1) / BM + p.G;  // upper bound of sum ceil(rows_g / BM)
+    long long mt;  // upper bound of the m-tile count (grouped: sum of ceil(rows_g / BM) <= R / BM + G)
+    if (p.offsets) mt = (p.max_rows + BM - 1) / BM + p.G;
     else mt = (long long)p.G * ((p.M_dense + BM - 1) / BM);
-    long long nb = 2LL * device_cus();
+    const long long cus = device_cus();
+    const int NTw = mode == GM_UP_SWIGLU ? (p.N + 255) / 256 : (p.N + WBN - 1) / WBN;
+    // the 128 x 512 tile pays off only with many rows per group (prefill); decode-sized groups
+    // (a few rows per expert) stream their weights better through the 128 x 128 tile
+    const long long rows_per_group = p.offsets ? p.max_rows / (p.G > 0 ? p.G : 1) : p.M_dense;
+    const bool wide = wide_ok() && mode != GM_DOWN_COMBINE && mode != GM_F32OUT && mt * NTw >= 2 * cus &&
+                      rows_per_group >= 64;
+    if (wide) {
+        // persistent grid: one workgroup per CU (the two operand stages fill the LDS)
+        long long nb = (mt * NTw + 7) / 8 * 8;
+        nb = nb < cus ? nb : cus;
+        nb = (nb + 7) / 8 * 8;
+        if (mode == GM_UP_SWIGLU) hipLaunchKernelGGL(k_gemm_bf16_wide8<GM_UP_SWIGLU>, dim3((unsigned)nb), dim3(512), 0, s, p, NTw);
+        else if (mode == GM_UP_RELU) hipLaunchKernelGGL(k_gemm_bf16_wide8<GM_UP_RELU>, dim3((unsigned)nb), dim3(512), 0, s, p, NTw);
+        else hipLaunchKernelGGL(k_gemm_bf16_wide8<GM_DOWN>, dim3((unsigned)nb), dim3(512), 0, s, p, NTw);
+        return hipGetLastError();
+    }
+    const int NT = mode == GM_UP_SWIGLU ? (p.N + 63) / 64 : (p.N + BN - 1) / BN;
+    // persistent grid: two workgroups per CU (LDS and registers allow two), a multiple of 8
+    long long nb = 2LL * cus;
     const long long need = (mt * NT + 7) / 8 * 8;
     nb = nb < need ? nb : need;
     nb = (nb + 7) / 8 * 8;
     if (mode == GM_UP_SWIGLU) hipLaunchKernelGGL(k_gemm_bf16<GM_UP_SWIGLU>, dim3((unsigned)nb), dim3(256), 0, s, p, NT);
     else if (mode == GM_UP_RELU) hipLaunchKernelGGL(k_gemm_bf16<GM_UP_RELU>, dim3((unsigned)nb), dim3(256), 0, s, p, NT);
     else if (mode == GM_DOWN) hipLaunchKernelGGL(k_gemm_bf16<GM_DOWN>, dim3((unsigned)nb), dim3(256), 0, s, p, NT);
+    else if (mode == GM_F32OUT) hipLaunchKernelGGL(k_gemm_bf16<GM_F32OUT>, dim3((unsigned)nb), dim3(256), 0, s, p, NT);
     else hipLaunchKernelGGL(k_gemm_bf16<GM_DOWN_COMBINE>, dim3((unsigned)nb), dim3(256), 0, s, p, NT);
     return hipGetLastError();
 }

@@ -34,7 +34,8 @@ hipError_t launch_gather(int dtype, const void* u, const int32_t* row_token, int
 // ---------------------------------------------------------------- expert FFN (grouped GEMM)
 // GM_DOWN_COMBINE: the shared experts' down GEMM whose epilogue also adds the residual and the
 // gate-weighted routed rows (Eq. 9) and writes the layer output.
-enum { GM_UP_SWIGLU = 0, GM_UP_RELU = 1, GM_DOWN = 2, GM_DOWN_COMBINE = 3 };
+// GM_F32OUT: plain product stored in fp32 (router logits).
+enum { GM_UP_SWIGLU = 0, GM_UP_RELU = 1, GM_DOWN = 2, GM_DOWN_COMBINE = 3, GM_F32OUT = 4 };
 
 struct GemmParams {
     const void* A;            // activation rows

@@ -77,6 +77,23 @@ hipError_t launch_logits(int dtype, const void* u, const void* e, float* logits,
         long long n = (long long)T * N;
         hipLaunchKernelGGL(k_logits_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, (const float*)u,
                            (const float*)e, logits, T, H, N);
+    } else if (T >= 1024 && N % 64 == 0) {
+        // prefill: the tiled MFMA GEMM (LDS-staged, fp32 output) over u [T, H] x e [N, H]^T
+        GemmParams p{};
+        p.A = u;
+        p.lda = H;
+        p.a_nrows = T;
+        p.B = e;
+        p.ldb = H;
+        p.K = H;
+        p.Kseg = H;
+        p.N = N;
+        p.M_dense = T;
+        p.G = 1;
+        p.max_rows = T;
+        p.C = logits;
+        p.ldc = N;
+        return launch_gemm(1, GM_F32OUT, p, s);
     } else if (T >= 2048) {
         dim3 grid((T + 63) / 64, (N + 63) / 64);
         hipLaunchKernelGGL(k_logits_bf16<4>, grid, dim3(256), 0, s, (const uint16_t*)u, (const uint16_t*)e,
