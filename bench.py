@@ -9,6 +9,9 @@ timing starts.  The decode regime (the first 128 tokens of the same inputs) is t
 Prints one JSON line.  Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -21,6 +24,11 @@ if ROOT not in sys.path:
 import numpy as np
 
 METRIC = "MoE-layer tokens/s and TFLOP/s (% bf16 MFMA peak) at V3-style shape; decode HBM GB/s"
+DOMINANT_KERNEL = "k_gemm_bf16_wide8<0, true>"   # routed gate/up grouped GEMM + SwiGLU
+KERNEL_SOURCES = ["fine_grained_shared_amd/csrc/ffn.hip", "fine_grained_shared_amd/csrc/kernels.hpp",
+                  "fine_grained_shared_amd/csrc/common.hpp"]
+TRAFFIC_FILE = "profiles/traffic_ffn_up_v3_prefill.json"
+COPY_BYTES = 1 << 30
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 
@@ -58,6 +66,99 @@ def decode_bytes(w, n_touched, T=None):
     e = 2 if w.dtype == 1 else 4
     per_expert = ffn_params(1, w.H, w.I, w.act == 1) * e
     return n_touched * per_expert + w.Ks * per_expert + w.N_r * w.H * e + 2 * T * w.H * e
+
+
+# ---------------------------------------------------------------- HBM traffic from rocprofv3 counters
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch of the dominant kernel from the committed counter summary, or None
+    when the kernel sources changed since the counters were taken."""
+    path = os.path.join(ROOT, TRAFFIC_FILE)
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        t = json.load(fh)
+    if t.get("source_sha256") != kernel_source_hash():
+        return None
+    return t.get("traffic_bytes_per_launch")
+
+
+def _read_counters(d):
+    """{kernel name: {counter: [per-dispatch values]}} from a rocprofv3 --pmc output directory."""
+    out = {}
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                name = r["Kernel_Name"]
+                key = (r.get("Dispatch_Id"), r["Counter_Name"])
+                out.setdefault(name, {}).setdefault(r["Counter_Name"], {}).setdefault(key, 0.0)
+                out[name][r["Counter_Name"]][key] += float(r["Counter_Value"])
+    return {k: {c: list(v.values()) for c, v in d2.items()} for k, d2 in out.items()}
+
+
+def _short(name):
+    n = name.split("(")[0]
+    return n.replace("void ", "").replace("moe::", "")
+
+
+def rocprof_summary(trace_dir, fetch_dir=None, write_dir=None, out_json=None):
+    """Markdown summary of a rocprofv3 --kernel-trace --stats run (and optional FETCH_SIZE /
+    WRITE_SIZE passes) for the profiles/ folder."""
+    lines = []
+    stats = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)
+    dom = None
+    for f in stats:
+        with open(f) as fh:
+            rows = list(csv.DictReader(fh))
+        lines.append("| kernel | calls | avg ms | total ms | % |")
+        lines.append("|---|---|---|---|---|")
+        for r in rows:
+            nm = _short(r["Name"])
+            avg = float(r["AverageNs"]) / 1e6
+            lines.append("| %s | %s | %.4f | %.3f | %.1f |" % (nm, r["Calls"], avg, float(r["TotalDurationNs"]) / 1e6,
+                                                              float(r["Percentage"])))
+            if nm.endswith(DOMINANT_KERNEL):
+                dom = avg
+    res = {"dominant_kernel": DOMINANT_KERNEL, "avg_ms": dom}
+    if fetch_dir and write_dir:
+        fc, wc = _read_counters(fetch_dir), _read_counters(write_dir)
+
+        def pick(cnt, pat, counter):
+            vals = [v for k, d in cnt.items() if pat in _short(k) for v in d.get(counter, [])]
+            return sum(vals) / len(vals) if vals else None
+
+        def copy_ref(cnt, counter):
+            # the 1 GiB device-to-device copy the bench issues before timing: the largest
+            # runtime copy-kernel dispatch
+            vals = [v for k, d in cnt.items() if "copyBuffer" in k for v in d.get(counter, [])]
+            return max(vals) if vals else None
+        copy_f = copy_ref(fc, "FETCH_SIZE")
+        copy_w = copy_ref(wc, "WRITE_SIZE")
+        k_f = pick(fc, DOMINANT_KERNEL, "FETCH_SIZE")
+        k_w = pick(wc, DOMINANT_KERNEL, "WRITE_SIZE")
+        if None not in (copy_f, copy_w, k_f, k_w):
+            sf, sw = COPY_BYTES / (copy_f * 1024), COPY_BYTES / (copy_w * 1024)
+            res.update({"copy_fetch_kib": copy_f, "copy_write_kib": copy_w, "fetch_kib_per_launch": k_f,
+                        "write_kib_per_launch": k_w, "fetch_scale": sf, "write_scale": sw,
+                        "traffic_bytes_per_launch": k_f * 1024 * sf + k_w * 1024 * sw,
+                        "source_sha256": kernel_source_hash()})
+            lines.append("")
+            lines.append("HBM traffic of %s per launch: FETCH_SIZE %.0f KiB x %.3f + WRITE_SIZE %.0f KiB x %.3f "
+                         "= %.3f GB (scales: a plain %d-byte device copy reads FETCH %.0f KiB / WRITE %.0f KiB)" % (
+                             DOMINANT_KERNEL, k_f, sf, k_w, sw, res["traffic_bytes_per_launch"] / 1e9, COPY_BYTES,
+                             copy_f, copy_w))
+    if out_json:
+        with open(out_json, "w") as fh:
+            json.dump(res, fh, indent=1)
+    return "\n".join(lines), res
 
 
 # ---------------------------------------------------------------- timing helpers
@@ -111,7 +212,7 @@ def _kernel_times(fn, steps):
     return res
 
 
-def cpu_baseline(w, inp, budget_s=15.0):
+def cpu_baseline(w, inp, budget_s=20.0):
     """The fp64 oracle on the host cores, on a bounded sample of the workload's tokens."""
     import oracle
     s = oracle.shape_of(w)
@@ -138,7 +239,15 @@ def main():
     ap.add_argument("--decode-tokens", type=int, default=128)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--rocprof-summary", metavar="TRACE_DIR", help="summarise a rocprofv3 run and exit")
+    ap.add_argument("--pmc-fetch", metavar="DIR")
+    ap.add_argument("--pmc-write", metavar="DIR")
+    ap.add_argument("--traffic-json", metavar="FILE")
     args = ap.parse_args()
+    if args.rocprof_summary:
+        text, _ = rocprof_summary(args.rocprof_summary, args.pmc_fetch, args.pmc_write, args.traffic_json)
+        print(text)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the layer runs data-parallel over tokens with replicated "
               "weights, so no exchange is needed and N>1 is not measured here (use --gpus 1).", file=sys.stderr)
@@ -201,9 +310,10 @@ def main():
                    "act": "SwiGLU", "parallelism": "single GPU"},
         "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
         "pct_bf16_peak": round(100 * flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
-        "roofline": {"kernel": "routed expert gate/up grouped GEMM + SwiGLU (k_gemm_bf16<UP_SWIGLU>)",
+        "roofline": {"kernel": "routed expert gate/up grouped GEMM + SwiGLU (%s)" % DOMINANT_KERNEL,
                      "bound": "mfma", "achieved": round(up_tflops, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(up_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(up_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic(),
                      "avg_launch_ms": round(up_ms, 4),
                      "algorithmic_flops_per_launch": routed_up_flops(w)},
         "kernels_ms_per_step": {k: round(v["ms_per_step"], 4) for k, v in kt.items()},

@@ -367,8 +367,9 @@ __device__ __forceinline__ int total_tiles(const GemmParams& p, int NT) {
     return p.G * ((p.M_dense + BM - 1) / BM) * NT;
 }
 
-template <int MODE>
+template <int MODE, bool GROUPED>
 __global__ __launch_bounds__(256, 2) void k_gemm_bf16(GemmParams p, int NT) {
+    if (GROUPED != (p.offsets != nullptr)) return;  // launched with the matching instantiation only
     __shared__ __attribute__((aligned(16))) unsigned char smem[kSmemBytes];
     const int total = total_tiles(p, NT);
     const int xcd = blockIdx.x & 7, loc = blockIdx.x >> 3, per_xcd = gridDim.x >> 3;
@@ -551,8 +552,9 @@ __device__ __forceinline__ void gemm_tile_wide8(const GemmParams& p, const TileI
     }
 }
 
-template <int MODE>
+template <int MODE, bool GROUPED>
 __global__ __launch_bounds__(512, 1) void k_gemm_bf16_wide8(GemmParams p, int NT) {
+    if (GROUPED != (p.offsets != nullptr)) return;  // launched with the matching instantiation only
     __shared__ __attribute__((aligned(16))) unsigned char smem[kWSmem];
     const int total = total_tiles(p, NT);
     const int xcd = blockIdx.x & 7, loc = blockIdx.x >> 3, per_xcd = gridDim.x >> 3;
@@ -652,9 +654,15 @@ hipError_t launch_gemm(int dtype, int mode, const GemmParams& p, hipStream_t s) 
         long long nb = (mt * NTw + 7) / 8 * 8;
         nb = nb < cus ? nb : cus;
         nb = (nb + 7) / 8 * 8;
-        if (mode == GM_UP_SWIGLU) hipLaunchKernelGGL(k_gemm_bf16_wide8<GM_UP_SWIGLU>, dim3((unsigned)nb), dim3(512), 0, s, p, NTw);
-        else if (mode == GM_UP_RELU) hipLaunchKernelGGL(k_gemm_bf16_wide8<GM_UP_RELU>, dim3((unsigned)nb), dim3(512), 0, s, p, NTw);
-        else hipLaunchKernelGGL(k_gemm_bf16_wide8<GM_DOWN>, dim3((unsigned)nb), dim3(512), 0, s, p, NTw);
+#define MOE_LAUNCH_W(M)                                                                                  \
+    do {                                                                                                 \
+        if (p.offsets) hipLaunchKernelGGL((k_gemm_bf16_wide8<M, true>), dim3((unsigned)nb), dim3(512), 0, s, p, NTw); \
+        else hipLaunchKernelGGL((k_gemm_bf16_wide8<M, false>), dim3((unsigned)nb), dim3(512), 0, s, p, NTw);    \
+    } while (0)
+        if (mode == GM_UP_SWIGLU) MOE_LAUNCH_W(GM_UP_SWIGLU);
+        else if (mode == GM_UP_RELU) MOE_LAUNCH_W(GM_UP_RELU);
+        else MOE_LAUNCH_W(GM_DOWN);
+#undef MOE_LAUNCH_W
         return hipGetLastError();
     }
     const int NT = mode == GM_UP_SWIGLU ? (p.N + 63) / 64 : (p.N + BN - 1) / BN;
@@ -663,11 +671,17 @@ hipError_t launch_gemm(int dtype, int mode, const GemmParams& p, hipStream_t s) 
     const long long need = (mt * NT + 7) / 8 * 8;
     nb = nb < need ? nb : need;
     nb = (nb + 7) / 8 * 8;
-    if (mode == GM_UP_SWIGLU) hipLaunchKernelGGL(k_gemm_bf16<GM_UP_SWIGLU>, dim3((unsigned)nb), dim3(256), 0, s, p, NT);
-    else if (mode == GM_UP_RELU) hipLaunchKernelGGL(k_gemm_bf16<GM_UP_RELU>, dim3((unsigned)nb), dim3(256), 0, s, p, NT);
-    else if (mode == GM_DOWN) hipLaunchKernelGGL(k_gemm_bf16<GM_DOWN>, dim3((unsigned)nb), dim3(256), 0, s, p, NT);
-    else if (mode == GM_F32OUT) hipLaunchKernelGGL(k_gemm_bf16<GM_F32OUT>, dim3((unsigned)nb), dim3(256), 0, s, p, NT);
-    else hipLaunchKernelGGL(k_gemm_bf16<GM_DOWN_COMBINE>, dim3((unsigned)nb), dim3(256), 0, s, p, NT);
+#define MOE_LAUNCH_N(M)                                                                                  \
+    do {                                                                                                 \
+        if (p.offsets) hipLaunchKernelGGL((k_gemm_bf16<M, true>), dim3((unsigned)nb), dim3(256), 0, s, p, NT); \
+        else hipLaunchKernelGGL((k_gemm_bf16<M, false>), dim3((unsigned)nb), dim3(256), 0, s, p, NT);    \
+    } while (0)
+    if (mode == GM_UP_SWIGLU) MOE_LAUNCH_N(GM_UP_SWIGLU);
+    else if (mode == GM_UP_RELU) MOE_LAUNCH_N(GM_UP_RELU);
+    else if (mode == GM_DOWN) MOE_LAUNCH_N(GM_DOWN);
+    else if (mode == GM_F32OUT) hipLaunchKernelGGL((k_gemm_bf16<GM_F32OUT, false>), dim3((unsigned)nb), dim3(256), 0, s, p, NT);
+    else hipLaunchKernelGGL((k_gemm_bf16<GM_DOWN_COMBINE, false>), dim3((unsigned)nb), dim3(256), 0, s, p, NT);
+#undef MOE_LAUNCH_N
     return hipGetLastError();
 }
 
