@@ -431,19 +431,27 @@ __device__ __forceinline__ void gemm_tile_wide8(const GemmParams& p, const TileI
         wrow0 = ti.nt * WBN + 64 * w + (lane >> 3);
         wrow_max = p.N - 1;
     }
-    auto dma_chunk = [&](int kt, int buf, int c) {   // c < 10: c < 2 -> A, else B chunk c - 2
-        const int k = kt * BK;
-        unsigned char* sa = smem + buf * kWStage;
+    // the two swizzle variants of this lane's B chunks (row 64 w + 8 i + lane/8: i even / odd)
+    const int kcgB0 = ((lane & 7) ^ ((lane >> 4) & 7)) * 8;
+    const int kcgB1 = ((lane & 7) ^ ((4 + (lane >> 4)) & 7)) * 8;
+    const unsigned ldb = (unsigned)p.ldb;
+    // DMA chunk c (< 10) of a k-tile whose A column offset is kA and B offset bo, into stage
+    // dst: c < 2 -> A chunk 2w + c, else B chunk 8w + (c - 2).  Per-k-step offsets are computed
+    // once by the caller; a chunk costs a clamp, one multiply-add and the M0 write.
+    auto dma_chunk = [&](int kA, long long bo, unsigned char* dst, int c) {
         if (c < 2) {
-            dma16(ag[c] + k, sa + (2 * w + c) * 1024);
+            dma16(ag[c] + kA, dst + (2 * w + c) * 1024);
         } else {
             const int i = c - 2;
-            const int seg = k / p.Kseg;
-            const long long bo = (long long)seg * p.sB_seg + (k - seg * p.Kseg);
             const int wr = min(wrow0 + 8 * i, wrow_max);
-            const int kcg = ((lane & 7) ^ ((4 * i + (lane >> 4)) & 7)) * 8;   // row = 64 w + 8 i + lane/8
-            dma16(Bg + (size_t)wr * p.ldb + kcg + bo, sa + kWTileA + (8 * w + i) * 1024);
+            dma16(Bg + ((size_t)(unsigned)wr * ldb + (unsigned)((i & 1) ? kcgB1 : kcgB0)) + bo,
+                  dst + kWTileA + (8 * w + i) * 1024);
         }
+    };
+    auto koffs = [&](int kt, int& kA, long long& bo) {
+        kA = kt * BK;
+        const int seg = kA / p.Kseg;
+        bo = (long long)seg * p.sB_seg + (kA - seg * p.Kseg);
     };
 
     f32x16 acc[4][2];
@@ -462,8 +470,13 @@ __device__ __forceinline__ void gemm_tile_wide8(const GemmParams& p, const TileI
     // wait + barrier sits before sub-step 3, which prefetches the next tile's fragments.
     bf16x8 af[2][4], bfr[2][2];
     __syncthreads();
+    {
+        int kA;
+        long long bo;
+        koffs(0, kA, bo);
 #pragma unroll
-    for (int c = 0; c < 10; ++c) dma_chunk(0, 0, c);
+        for (int c = 0; c < 10; ++c) dma_chunk(kA, bo, smem, c);
+    }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 #pragma unroll
@@ -474,7 +487,10 @@ __device__ __forceinline__ void gemm_tile_wide8(const GemmParams& p, const TileI
         const int buf = kt & 1;
         const int kn = kt + 1 < nk ? kt + 1 : kt;
         const unsigned char* sa = smem + buf * kWStage;
-        const unsigned char* na = smem + (buf ^ 1) * kWStage;
+        unsigned char* na = smem + (buf ^ 1) * kWStage;
+        int kA;
+        long long bo;
+        koffs(kn, kA, bo);
 #pragma unroll
         for (int s = 0; s < BK / 16; ++s) {
             const int cur = s & 1;
@@ -494,8 +510,8 @@ __device__ __forceinline__ void gemm_tile_wide8(const GemmParams& p, const TileI
                 if (g < 2) bfr[cur ^ 1][g] = frag(fa + kWTileA, brow[g] + (lane & 31), kc);
                 if (s < 2) {
                     const int c = 5 * s + g;
-                    dma_chunk(kn, buf ^ 1, c);
-                    if (g == 3) dma_chunk(kn, buf ^ 1, c + 1);
+                    dma_chunk(kA, bo, na, c);
+                    if (g == 3) dma_chunk(kA, bo, na, c + 1);
                 }
             }
         }
