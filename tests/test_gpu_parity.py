@@ -306,3 +306,56 @@ def test_bias_update_bit_exact(ragged, torch_cuda):
         assert np.array_equal(counts.cpu().numpy(), ref_counts)
         b_host = oracle.bias_update(w.N_r, w.T, w.K_r, ref_counts, 0.01, b_host)
         assert np.array_equal(bias.cpu().numpy(), b_host)
+
+
+def test_profile_api_counts_launches(ragged, torch_cuda):
+    import fine_grained_shared_amd as moe
+    torch = torch_cuda
+    torch.cuda.synchronize()
+    moe.moe_profile_enable(True)
+    for _ in range(3):
+        ragged.forward()
+    torch.cuda.synchronize()
+    moe.moe_profile_enable(False)
+    n_up, ms_up = moe.moe_profile_query(moe.MOE_PROF_FFN_UP)
+    n_rt, ms_rt = moe.moe_profile_query(moe.MOE_PROF_ROUTER)
+    assert n_up == 3 and ms_up > 0.0          # one routed up launch per layer call
+    assert n_rt == 6 and ms_rt > 0.0          # logits + selection per call
+    with pytest.raises(moe.MoeError):
+        moe.moe_profile_query(99)
+
+
+def test_graph_capture_replays_match_eager(ragged, torch_cuda):
+    """The layer only enqueues work (no host sync, no memset): it can be captured in a HIP graph.
+    Replays, with eager work between them, must reproduce the eager output bit for bit."""
+    import fine_grained_shared_amd as moe
+    torch = torch_cuda
+    w, d = ragged.w, ragged.dev
+    s = gpu_shape(w)
+    ws = moe.workspace(s)
+    out = torch.empty((w.T, w.H), dtype=torch.bfloat16, device="cuda")
+    idx = torch.empty((w.T, w.K_r), dtype=torch.int32, device="cuda")
+    wts = torch.empty((w.T, w.K_r), dtype=torch.float32, device="cuda")
+
+    def run():
+        moe.moe_layer_forward(s, d["u"], d["centroids"], d["bias"], d["w1"], None, d["w2"], d["w1_sh"], None,
+                              d["w2_sh"], 0, out, idx, wts, ws)
+    run()
+    torch.cuda.synchronize()
+    ref = out.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()   # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    for i in range(4):
+        out.zero_()
+        ragged.forward()          # eager work on other buffers between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), "replay %d differs from eager" % i
