@@ -24,7 +24,7 @@ if ROOT not in sys.path:
 import numpy as np
 
 METRIC = "MoE-layer tokens/s and TFLOP/s (% bf16 MFMA peak) at V3-style shape; decode HBM GB/s"
-DOMINANT_KERNEL = "k_gemm_bf16_wide8<0, true>"   # routed gate/up grouped GEMM + SwiGLU
+DOMINANT_KERNEL = "k_gemm_bf16_w4<0, true>"   # routed gate/up grouped GEMM + SwiGLU
 KERNEL_SOURCES = ["fine_grained_shared_amd/csrc/ffn.hip", "fine_grained_shared_amd/csrc/kernels.hpp",
                   "fine_grained_shared_amd/csrc/common.hpp"]
 TRAFFIC_FILE = "profiles/traffic_ffn_up_v3_prefill.json"

@@ -6,10 +6,17 @@
 //   SwiGLU: y = W2 (SiLU(Wg x) * (Wu x))      ReLU: y = V ReLU(W x + b)   (tomabc explainer)
 // computed as an "up" GEMM with the activation fused into its epilogue, then a "down" GEMM.
 //
-// bf16 path: 128 x 128 x 64 workgroup tiles, 4 waves of 64 x 64 on v_mfma_f32_32x32x16_bf16,
-// operands staged through double-buffered LDS.  For SwiGLU the 128 weight rows of a tile are
-// 64 gate rows and the 64 matching up rows, so the epilogue has both halves of every output
-// element in the same lane.  fp32 path: plain VALU kernels (the tiny fp32 layer only).
+// bf16 path, all on v_mfma_f32_32x32x16_bf16 with persistent XCD-aware grids and operands in
+// double-buffered LDS:
+//  - 128 x 512 x 64 tiles, four waves of 128 x 128, operands register-staged with buffer loads
+//    (the prefill GEMMs: many rows per group);
+//  - 128 x 512 x 64 tiles, eight waves of 128 x 64, direct-to-LDS loads (the same GEMMs when an
+//    operand spans 2 GiB or more);
+//  - 128 x 128 x 64 tiles, four waves of 64 x 64, two workgroups per CU (decode-sized groups,
+//    the fused shared-down + combine, the router logits).
+// For SwiGLU the weight rows of a tile are gate rows and the matching up rows, so the epilogue
+// has both halves of every output element in the same lane.  fp32 path: plain VALU kernels (the
+// tiny fp32 layer only).
 #include <stdlib.h>
 
 #include "common.hpp"
@@ -21,16 +28,19 @@ constexpr int BM = 128, BN = 128, BK = 64;
 
 int gemm_bm(int dtype) { return dtype == 0 ? 1 : BM; }
 
-// The wide-tile kernel can be switched off with MOE_GEMM_WIDE=0 (for A/B measurements).
-static bool wide_ok() {
+// Wide-tile kernel selection for A/B measurements: MOE_GEMM_WIDE=0 (128 x 128 tiles only),
+// =dma (128 x 512 tiles staged with direct-to-LDS loads); default: 128 x 512 tiles staged through
+// registers with buffer loads (the direct-to-LDS kernel serves operands spanning 2 GiB or more).
+static int wide_mode() {
     static int v = -1;
     if (v < 0) {
         const char* e = getenv("MOE_GEMM_WIDE");
-        v = (e && e[0] == '0') ? 0 : 1;
+        v = 2;
+        if (e && e[0] == '0') v = 0;
+        else if (e && e[0] == 'd') v = 1;
     }
-    return v == 1;
+    return v;
 }
-
 
 // Compute units of the current device (cached per device id).
 static int device_cus() {
@@ -399,6 +409,61 @@ __device__ __forceinline__ const bf16x8& frag(const unsigned char* base, int row
     return *reinterpret_cast<const bf16x8*>(base + row * 128 + ((kc ^ ((row >> 1) & 7)) << 4));
 }
 
+// Epilogue of a 128 x 512 tile held as acc[i][j] (rows 32 i.., columns of wave w: SwiGLU gate / up
+// blocks 32 w and 256 + 32 w, otherwise 64 w + 32 j): stage through LDS, 16-byte stores.
+template <int MODE>
+__device__ __forceinline__ void wide_epilogue(const GemmParams& p, const TileInfo& ti, f32x16 (&acc)[4][2],
+                                              unsigned char* smem) {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, w = tid >> 6;
+    float* st = reinterpret_cast<float*>(smem);
+    if (MODE == GM_UP_SWIGLU) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const int rl = 32 * i + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+                st[rl * WEPW_SW + 32 * w + (lane & 31)] = silu(acc[i][0][q]) * acc[i][1][q];
+            }
+        __syncthreads();
+        const int cq = (tid & 31) * 8;
+        const int col0 = ti.nt * 256 + cq;
+        if (col0 < p.N) {
+            for (int rl = tid >> 5; rl < ti.rows; rl += 16) {
+                const float4 v0 = *reinterpret_cast<const float4*>(&st[rl * WEPW_SW + cq]);
+                const float4 v1 = *reinterpret_cast<const float4*>(&st[rl * WEPW_SW + cq + 4]);
+                float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+                epilogue_row<MODE>(p, ti, v, rl, col0);
+            }
+        }
+        return;
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {   // rows [64 h, 64 h + 64)
+        if (h) __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                    const int rl = 32 * i + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+                    st[rl * WEPW + 64 * w + 32 * j + (lane & 31)] = acc[2 * h + i][j][q];
+                }
+        __syncthreads();
+        const int cq = lane * 8;
+        const int col0 = ti.nt * WBN + cq;
+        if (col0 < p.N) {
+            for (int rl = w; rl < 64 && 64 * h + rl < ti.rows; rl += 8) {
+                const float4 v0 = *reinterpret_cast<const float4*>(&st[rl * WEPW + cq]);
+                const float4 v1 = *reinterpret_cast<const float4*>(&st[rl * WEPW + cq + 4]);
+                float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+                epilogue_row<MODE>(p, ti, v, 64 * h + rl, col0);
+            }
+        }
+    }
+}
+
 // Eight waves (two per SIMD), each owning a 128 x 64 block (4 x 2 accumulators).  Issue is in
 // order, and a DMA issue stalls its wave for tens of cycles while the CU's address unit is busy;
 // the other wave of the SIMD keeps the matrix pipe fed meanwhile.
@@ -518,54 +583,7 @@ __device__ __forceinline__ void gemm_tile_wide8(const GemmParams& p, const TileI
         __builtin_amdgcn_sched_barrier(0);
     }
     __syncthreads();
-
-    // ---- epilogue
-    float* st = reinterpret_cast<float*>(smem);
-    if (MODE == GM_UP_SWIGLU) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int q = 0; q < 16; ++q) {
-                const int rl = 32 * i + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
-                st[rl * WEPW_SW + 32 * w + (lane & 31)] = silu(acc[i][0][q]) * acc[i][1][q];
-            }
-        __syncthreads();
-        const int cq = (tid & 31) * 8;
-        const int col0 = ti.nt * 256 + cq;
-        if (col0 < p.N) {
-            for (int rl = tid >> 5; rl < ti.rows; rl += 16) {
-                const float4 v0 = *reinterpret_cast<const float4*>(&st[rl * WEPW_SW + cq]);
-                const float4 v1 = *reinterpret_cast<const float4*>(&st[rl * WEPW_SW + cq + 4]);
-                float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-                epilogue_row<MODE>(p, ti, v, rl, col0);
-            }
-        }
-        return;
-    }
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {   // rows [64 h, 64 h + 64)
-        if (h) __syncthreads();
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-#pragma unroll
-                for (int q = 0; q < 16; ++q) {
-                    const int rl = 32 * i + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
-                    st[rl * WEPW + 64 * w + 32 * j + (lane & 31)] = acc[2 * h + i][j][q];
-                }
-        __syncthreads();
-        const int cq = lane * 8;
-        const int col0 = ti.nt * WBN + cq;
-        if (col0 < p.N) {
-            for (int rl = w; rl < 64 && 64 * h + rl < ti.rows; rl += 8) {
-                const float4 v0 = *reinterpret_cast<const float4*>(&st[rl * WEPW + cq]);
-                const float4 v1 = *reinterpret_cast<const float4*>(&st[rl * WEPW + cq + 4]);
-                float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-                epilogue_row<MODE>(p, ti, v, 64 * h + rl, col0);
-            }
-        }
-    }
+    wide_epilogue<MODE>(p, ti, acc, smem);
 }
 
 template <int MODE, bool GROUPED>
@@ -580,6 +598,256 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16_wide8(GemmParams p, int NT
         TileInfo ti;
         decode_tile(p, NT, BM, L, ti);
         gemm_tile_wide8<MODE>(p, ti, smem);
+    }
+}
+
+// LDS hand-off without waiting for outstanding global loads: LDS-op wait plus workgroup barrier.
+// The empty asm statements keep the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt not waited for
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// ---------------------------------------------------------------- 4-wave 128 x 512 tile
+// Four waves (one per SIMD), each owning a 128 x 128 block of the 128 x 512 tile (4 x 4
+// accumulators of 32 x 32 in the accumulator registers).  Per k-step each wave reads all 128 A
+// rows and its own 128 B rows from LDS: 128 KB of fragment reads per workgroup, against 192 KB
+// for eight waves of 128 x 64.  Operands are staged through registers: per k-step a wave loads
+// 20 chunks of 1 KB (A chunks 4w .. 4w+3, B chunks 16w .. 16w+15) with 16-byte buffer loads for
+// k-tile kt+2 while k-step kt computes, and stores them to the free LDS stage during k-step
+// kt+1, so a load has a whole k-step to land and the only hand-off per k-step is an LDS-store
+// wait plus barrier.
+// SwiGLU: B rows [128 w, 128 w + 64) of the tile are gate rows n0 + 64 w + t and rows
+// [128 w + 64, 128 w + 128) the matching up rows, so wave w produces output columns
+// n0 + 64 w .. n0 + 64 w + 63 from accumulator pairs (j, j + 2).
+constexpr int W4EPW = WBN + 4;   // non-SwiGLU staging row (512 outputs, 64 rows per pass)
+
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+
+// Buffer resource over [ptr, ptr + bytes) for 16-byte loads with a per-lane 32-bit byte offset and a
+// wave-uniform scalar byte offset.  The base is made wave-uniform explicitly.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* ptr, int bytes) {
+    const unsigned long long a = (unsigned long long)ptr;
+    const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)a);
+    const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(a >> 32));
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(((unsigned long long)hi << 32) | lo), (short)0, bytes,
+                                             0x00020000);
+}
+
+template <int MODE>
+__device__ __forceinline__ void gemm_tile_w4(const GemmParams& p, const TileInfo& ti, unsigned char* smem) {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, w = tid >> 6;   // w < 4
+
+    // Operands are read with buffer loads: a constant per-lane byte offset per chunk and a scalar
+    // k-step offset, so a k-step needs no vector address arithmetic.  A spans p.a_bytes and one
+    // group's weights p.b_bytes (both below 2^31).
+    const __amdgpu_buffer_rsrc_t rsA = make_rsrc(p.A, p.a_bytes);
+    const __amdgpu_buffer_rsrc_t rsB =
+        make_rsrc((const uint16_t*)p.B + (size_t)ti.g * p.sB_group, p.b_bytes);
+    // 16-byte chunk permutation of a lane for chunk parity 0 / 1 (rows 8 i + lane / 8 of an
+    // 8-row chunk whose first row is a multiple of 16 for even i)
+    const int kcg0 = ((lane & 7) ^ ((lane >> 4) & 7)) * 8;
+    const int kcg1 = ((lane & 7) ^ ((4 + (lane >> 4)) & 7)) * 8;
+    unsigned voA[4];    // byte offset of A chunk 4w + i of this lane (k-tile 0)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = 32 * w + 8 * i + (lane >> 3);
+        const int r = min(row, ti.rows - 1);
+        long long src = ti.row0 + r;
+        if (p.a_rows) src = min(max((long long)p.a_rows[src], 0LL), p.a_nrows - 1);
+        voA[i] = (unsigned)(src * p.lda + ((i & 1) ? kcg1 : kcg0)) * 2u;
+    }
+    unsigned voB[16];   // byte offset of B chunk 16w + i of this lane within the group's weights
+    {
+        const unsigned ldb = (unsigned)p.ldb;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            int wr;
+            if (MODE == GM_UP_SWIGLU) {
+                const int t = 64 * w + 8 * (i & 7) + (lane >> 3);
+                wr = i < 8 ? min(ti.nt * 256 + t, p.N - 1) : p.up_off + min(ti.nt * 256 + t, p.N - 1);
+            } else {
+                wr = min(ti.nt * WBN + 128 * w + 8 * i + (lane >> 3), p.N - 1);
+            }
+            voB[i] = ((unsigned)wr * ldb + (unsigned)((i & 1) ? kcg1 : kcg0)) * 2u;
+        }
+    }
+    const int la = (4 * w) * 1024 + lane * 16;              // A chunk 4w of this lane in a stage
+    const int lb = kWTileA + (16 * w) * 1024 + lane * 16;   // B chunk 16w
+    const int nk = p.K / BK;
+
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+    const int brow0 = 128 * w + (lane & 31);
+
+    // staging registers: one named variable per chunk (an array of them is not kept in registers)
+    v4u r0, r1, r2, r3, r4, r5, r6, r7, r8, r9, r10, r11, r12, r13, r14, r15, r16, r17, r18, r19;
+#define MOE_W4_LD(C, RV)                                                             \
+    RV = (C) < 4 ? __builtin_amdgcn_raw_buffer_load_b128(rsA, voA[(C) & 3], soA, 0) \
+                 : __builtin_amdgcn_raw_buffer_load_b128(rsB, voB[((C) - 4) & 15], soB, 0)
+#define MOE_W4_ST(D, C, RV) \
+    *reinterpret_cast<v4u*>((D) + ((C) < 4 ? la + (C) * 1024 : lb + ((C) - 4) * 1024)) = RV
+#define MOE_W4_ALL(OP)                                                                          \
+    OP(0, r0); OP(1, r1); OP(2, r2); OP(3, r3); OP(4, r4); OP(5, r5); OP(6, r6); OP(7, r7);     \
+    OP(8, r8); OP(9, r9); OP(10, r10); OP(11, r11); OP(12, r12); OP(13, r13); OP(14, r14);      \
+    OP(15, r15); OP(16, r16); OP(17, r17); OP(18, r18); OP(19, r19)
+#define MOE_W4_ST0(C, RV) MOE_W4_ST(smem, C, RV)
+#define MOE_W4_SL(C, RV)     \
+    case C:                  \
+        MOE_W4_ST(na, C, RV); \
+        MOE_W4_LD(C, RV);     \
+        break
+    // scalar byte offsets of the k-tile loaded next: A column kA, B offset (segment base + rem)
+    int soA = 0, soB = 0, rem = 0, segb = 0;
+    const int kseg2 = 2 * p.Kseg, sseg2 = (int)(2 * p.sB_seg);
+    auto advance = [&]() {   // to the next k-tile
+        soA += 2 * BK;
+        rem += 2 * BK;
+        if (rem == kseg2) {
+            rem = 0;
+            segb += sseg2;
+        }
+        soB = segb + rem;
+    };
+
+    __syncthreads();   // the previous tile's epilogue may still read the LDS staging area
+    MOE_W4_ALL(MOE_W4_LD);
+    MOE_W4_ALL(MOE_W4_ST0);
+    if (nk > 1) advance();
+    MOE_W4_ALL(MOE_W4_LD);
+    lds_barrier();
+    bf16x8 af[2][4], bfr[2][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) af[0][i] = frag(smem, 32 * i + (lane & 31), lane >> 5);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bfr[0][j] = frag(smem + kWTileA, brow0 + 32 * j, lane >> 5);
+
+    // k-step kt (stage b = kt & 1), four sub-steps of 16 MFMAs in 8 fenced groups of two; groups
+    // 0-3 also issue two fragment reads for the next sub-step and, in sub-steps 0-2, groups 0-6
+    // the LDS store of one chunk of k-tile kt+1 (registers -> stage b^1) followed by the global
+    // load of the same chunk of k-tile kt+2.  LDS-store wait + barrier before sub-step 3, whose
+    // fragment reads come from stage b^1.
+    for (int kt = 0; kt < nk; ++kt) {
+        const int buf = kt & 1;
+        const unsigned char* sa = smem + buf * kWStage;
+        unsigned char* na = smem + (buf ^ 1) * kWStage;
+        if (kt + 2 < nk) advance();   // this k-step loads k-tile min(kt + 2, nk - 1)
+#pragma unroll
+        for (int s = 0; s < BK / 16; ++s) {
+            const int cur = s & 1;
+            if (s == 3) {
+                __builtin_amdgcn_sched_barrier(0);
+                lds_barrier();
+            }
+            const unsigned char* fa = s < 3 ? sa : na;
+            const int kc = 2 * ((s + 1) & 3) + (lane >> 5);
+#pragma unroll
+            for (int g = 0; g < 8; ++g) {
+                // one wave per SIMD issues in order, and an MFMA waits for the matrix pipe: each
+                // MFMA of the pair is followed by its own fenced window of other work (the chunk
+                // staging after the first, the fragment read after the second), which issues while
+                // that MFMA executes
+                const int i = g >> 1, j0 = 2 * (g & 1);
+                __builtin_amdgcn_sched_barrier(0);
+                acc[i][j0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bfr[cur][j0], acc[i][j0], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+                const int c = 7 * s + g;   // chunk staged by this group
+                if (s < 3 && g < 7 && c < 20) {
+                    switch (c) { MOE_W4_ALL(MOE_W4_SL); }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                acc[i][j0 + 1] =
+                    __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bfr[cur][j0 + 1], acc[i][j0 + 1], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+                // fragment reads for the next sub-step, all in the first four groups (their
+                // registers were last read by the previous sub-step), so they have landed long
+                // before the next sub-step's first MFMA
+                if (g < 4) {
+                    bfr[cur ^ 1][g] = frag(fa + kWTileA, brow0 + 32 * g, kc);
+                    af[cur ^ 1][g] = frag(fa, 32 * g + (lane & 31), kc);
+                }
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+#undef MOE_W4_LD
+#undef MOE_W4_ST
+#undef MOE_W4_ALL
+#undef MOE_W4_ST0
+#undef MOE_W4_SL
+    __syncthreads();
+
+    // ---- epilogue: stage through LDS, 16-byte stores
+    float* st = reinterpret_cast<float*>(smem);
+    if (MODE == GM_UP_SWIGLU) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                    const int rl = 32 * i + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+                    st[rl * WEPW_SW + 64 * w + 32 * jj + (lane & 31)] = silu(acc[i][jj][q]) * acc[i][jj + 2][q];
+                }
+        __syncthreads();
+        const int cq = (tid & 31) * 8;
+        const int col0 = ti.nt * 256 + cq;
+        if (col0 < p.N) {
+            for (int rl = tid >> 5; rl < ti.rows; rl += 8) {
+                const float4 v0 = *reinterpret_cast<const float4*>(&st[rl * WEPW_SW + cq]);
+                const float4 v1 = *reinterpret_cast<const float4*>(&st[rl * WEPW_SW + cq + 4]);
+                float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+                epilogue_row<MODE>(p, ti, v, rl, col0);
+            }
+        }
+        return;
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {   // rows [64 h, 64 h + 64)
+        if (h) __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                    const int rl = 32 * i + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+                    st[rl * W4EPW + 128 * w + 32 * j + (lane & 31)] = acc[2 * h + i][j][q];
+                }
+        __syncthreads();
+        const int cq = lane * 8;
+        const int col0 = ti.nt * WBN + cq;
+        if (col0 < p.N) {
+            for (int rl = w; rl < 64 && 64 * h + rl < ti.rows; rl += 4) {
+                const float4 v0 = *reinterpret_cast<const float4*>(&st[rl * W4EPW + cq]);
+                const float4 v1 = *reinterpret_cast<const float4*>(&st[rl * W4EPW + cq + 4]);
+                float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+                epilogue_row<MODE>(p, ti, v, 64 * h + rl, col0);
+            }
+        }
+    }
+}
+
+template <int MODE, bool GROUPED>
+__global__ __launch_bounds__(256, 1) void k_gemm_bf16_w4(GemmParams p, int NT) {
+    if (GROUPED != (p.offsets != nullptr)) return;  // launched with the matching instantiation only
+    __shared__ __attribute__((aligned(16))) unsigned char smem[kWSmem];
+    const int total = total_tiles(p, NT);
+    const int xcd = blockIdx.x & 7, loc = blockIdx.x >> 3, per_xcd = gridDim.x >> 3;
+    const int beg = (int)((long long)total * xcd / 8);
+    const int end = (int)((long long)total * (xcd + 1) / 8);
+    for (int L = beg + loc; L < end; L += per_xcd) {
+        TileInfo ti;
+        decode_tile(p, NT, BM, L, ti);
+        gemm_tile_w4<MODE>(p, ti, smem);
     }
 }
 
@@ -644,8 +912,19 @@ __global__ __launch_bounds__(256) void k_gemm_f32(GemmParams p) {
     }
 }
 
-hipError_t launch_gemm(int dtype, int mode, const GemmParams& p, hipStream_t s) {
+hipError_t launch_gemm(int dtype, int mode, const GemmParams& p_in, hipStream_t s) {
+    GemmParams p = p_in;
     if (p.G == 0 || p.max_rows == 0 || p.N == 0) return hipSuccess;
+    {
+        // byte spans for 32-bit buffer offsets: A rows reachable by the row space, one group's weights
+        const long long a_rows_n = p.a_rows ? p.a_nrows : (p.offsets ? (long long)p.max_rows : (long long)p.M_dense);
+        const long long a_span = a_rows_n * p.lda * 2;
+        const long long b_rows = mode == GM_UP_SWIGLU ? (long long)p.up_off + p.N : (long long)p.N;
+        const long long b_span = ((long long)(p.K / (p.Kseg > 0 ? p.Kseg : 1)) - 1) * p.sB_seg * 2 + b_rows * p.ldb * 2;
+        const long long lim = 0x7FFFFFF0LL;
+        p.a_bytes = a_span > 0 && a_span < lim ? (int)a_span : 0;
+        p.b_bytes = b_span > 0 && b_span < lim ? (int)b_span : 0;
+    }
     if (dtype == 0) {
         if (mode == GM_DOWN_COMBINE || mode == GM_F32OUT) return hipErrorInvalidValue;  // bf16 modes only
         dim3 grid((p.N + 63) / 64, (p.max_rows + 3) / 4, p.offsets ? 1 : p.G);
@@ -663,17 +942,36 @@ hipError_t launch_gemm(int dtype, int mode, const GemmParams& p, hipStream_t s) 
     // the 128 x 512 tile pays off only with many rows per group (prefill); decode-sized groups
     // (a few rows per expert) stream their weights better through the 128 x 128 tile
     const long long rows_per_group = p.offsets ? p.max_rows / (p.G > 0 ? p.G : 1) : p.M_dense;
-    const bool wide = wide_ok() && mode != GM_DOWN_COMBINE && mode != GM_F32OUT && mt * NTw >= 2 * cus &&
-                      rows_per_group >= 64;
+    // buffer-load kernel: the plain modes and fp32 output (its epilogue is the shared per-row one);
+    // direct-to-LDS kernel: the plain modes, for operands too large for 32-bit buffer offsets.
+    // The fused combine stays on the 128 x 128 tiles: its epilogue gathers K_r routed rows per
+    // output row, and two workgroups per CU overlap that gather with the other's MFMAs.
+    const bool w4 = wide_mode() == 2 && p.a_bytes > 0 && p.b_bytes > 0;
+    const bool wide = wide_mode() != 0 && mode != GM_DOWN_COMBINE && (w4 || mode != GM_F32OUT) &&
+                      mt * NTw >= 2 * cus && rows_per_group >= 64;
     if (wide) {
         // persistent grid: one workgroup per CU (the two operand stages fill the LDS)
         long long nb = (mt * NTw + 7) / 8 * 8;
         nb = nb < cus ? nb : cus;
         nb = (nb + 7) / 8 * 8;
+        const dim3 grid((unsigned)nb);
+        if (w4) {
+#define MOE_LAUNCH_W4(M)                                                                        \
+    do {                                                                                        \
+        if (p.offsets) hipLaunchKernelGGL((k_gemm_bf16_w4<M, true>), grid, dim3(256), 0, s, p, NTw); \
+        else hipLaunchKernelGGL((k_gemm_bf16_w4<M, false>), grid, dim3(256), 0, s, p, NTw);    \
+    } while (0)
+            if (mode == GM_UP_SWIGLU) MOE_LAUNCH_W4(GM_UP_SWIGLU);
+            else if (mode == GM_UP_RELU) MOE_LAUNCH_W4(GM_UP_RELU);
+            else if (mode == GM_DOWN) MOE_LAUNCH_W4(GM_DOWN);
+            else hipLaunchKernelGGL((k_gemm_bf16_w4<GM_F32OUT, false>), grid, dim3(256), 0, s, p, NTw);
+#undef MOE_LAUNCH_W4
+            return hipGetLastError();
+        }
 #define MOE_LAUNCH_W(M)                                                                                  \
     do {                                                                                                 \
-        if (p.offsets) hipLaunchKernelGGL((k_gemm_bf16_wide8<M, true>), dim3((unsigned)nb), dim3(512), 0, s, p, NTw); \
-        else hipLaunchKernelGGL((k_gemm_bf16_wide8<M, false>), dim3((unsigned)nb), dim3(512), 0, s, p, NTw);    \
+        if (p.offsets) hipLaunchKernelGGL((k_gemm_bf16_wide8<M, true>), grid, dim3(512), 0, s, p, NTw); \
+        else hipLaunchKernelGGL((k_gemm_bf16_wide8<M, false>), grid, dim3(512), 0, s, p, NTw);    \
     } while (0)
         if (mode == GM_UP_SWIGLU) MOE_LAUNCH_W(GM_UP_SWIGLU);
         else if (mode == GM_UP_RELU) MOE_LAUNCH_W(GM_UP_RELU);

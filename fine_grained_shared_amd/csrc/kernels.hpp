@@ -67,6 +67,10 @@ struct GemmParams {
     const float* topk_w;      // [M_dense, K_r]
     int K_r;
     long long R;
+    // set by launch_gemm: byte spans of A and of one group's weights when both are below 2^31
+    // (kernels addressing them with 32-bit buffer offsets are chosen only then), else 0
+    int a_bytes;
+    int b_bytes;
 };
 // m-tile prefix of the groups defined by offsets (grouped mode), for tiles of bm rows
 hipError_t launch_tile_plan(const int32_t* offsets, int G, int bm, int32_t* tiles, hipStream_t s);

@@ -1,0 +1,36 @@
+"""GPU parity when the activations span more than 2 GiB: T=152000 tokens of H=7168 bf16
+(2.18 GB), 8 routed experts top-2 + 1 shared, I=256, sigmoid + selection bias.
+
+The projections that read the activations (routed and shared up) cannot use 32-bit buffer
+offsets there and run on the 128 x 512 kernel with 64-bit addressing and direct-to-LDS loads;
+the down projections (the shared one with the fused combine) read the 156 MB / 78 MB hidden
+activations and stay on the buffer-load kernel.  The layer output is checked on a sample of
+tokens against the oracle, routing on the same sample.
+"""
+import gc
+
+import numpy as np
+import pytest
+
+import synth
+from parity_util import Case, layer_parity, sample_tokens, say
+
+pytestmark = pytest.mark.gpu
+
+
+def test_activations_beyond_2gib():
+    import torch
+    assert torch.cuda.is_available()
+    w = synth.Workload("big_u", "T=152000 H=7168 bf16 activations (2.18 GB), 8 routed top-2 + 1 shared, I=256",
+                       152000, 7168, 8, 2, 1, 256, synth.GATE_SIGMOID_BIAS_NORM, synth.ACT_SWIGLU, synth.DT_BF16,
+                       bias_var=0.01)
+    assert w.T * w.H * 2 > 2 ** 31
+    say("[large] generating %.2f GB of activations" % (w.T * w.H * 2 / 1e9))
+    case = Case(w)
+    try:
+        layer_parity(case, tokens=sample_tokens(w.T, 48), route_all=False, label="big_u")
+    finally:
+        case.dev.clear()
+        case.inp.clear()
+        gc.collect()
+        torch.cuda.empty_cache()
