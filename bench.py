@@ -193,6 +193,51 @@ def _time_steps(fn, steps, warmup):
     return a.elapsed_time(b) / steps
 
 
+def _step_stats(fn, steps):
+    """Median / min / max of single-step times (events around each step on the current stream)."""
+    import torch
+    st = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record(st)
+    for i in range(steps):
+        fn()
+        ev[i + 1].record(st)
+    torch.cuda.synchronize()
+    t = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)])
+    return {"median": round(float(np.median(t)), 4), "min": round(float(t.min()), 4), "max": round(float(t.max()), 4)}
+
+
+def _copy_gbs(nbytes=1 << 30, reps=5):
+    """Device-to-device copy bandwidth (read + write bytes per second): HBM context for decode."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    del src, dst
+    return 2.0 * nbytes / (ms * 1e-3) / 1e9
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def _kernel_times(fn, steps):
     """Average duration per launch of each kernel class, from HIP events the library records
     on the launch stream around every kernel."""
@@ -227,7 +272,8 @@ def cpu_baseline(w, inp, budget_s=20.0):
     dt = time.time() - t0
     return {"value": round(n / dt, 3), "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
             "sample": "%d of %d tokens (evenly strided) of the same layer, full forward in fp64, %.1f s" % (
-                n, w.T, dt)}
+                n, w.T, dt),
+            "cpu_model": _cpu_model(), "fp64_gflops": round(layer_flops(w) / w.T * n / dt / 1e9, 2)}
 
 
 def main():
@@ -285,6 +331,7 @@ def main():
 
     ms = _time_steps(step, args.steps, args.warmup)
     print("[bench] prefill %.3f ms/step" % ms, file=sys.stderr, flush=True)
+    stats = _step_stats(step, args.steps)
     kt = _kernel_times(step, max(2, min(args.steps, 10)))
     flops = layer_flops(w)
     up = kt.get("ffn_up", {"ms_per_step": float("nan"), "launches_per_step": 1})
@@ -300,6 +347,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "step_ms": stats,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -336,13 +384,16 @@ def main():
                                   d["b1_sh"], d["w2_sh"], 0, outd, idxd, wtd, wsd)
 
         dms = _time_steps(dstep, max(args.steps, 10), args.warmup)
+        dstats = _step_stats(dstep, max(args.steps, 10))
         dkt = _kernel_times(dstep, 10)
+        copy = _copy_gbs()
         touched = int(np.unique(idxd.cpu().numpy()).size)
         nbytes = decode_bytes(wd, touched)
         gbs = nbytes / (dms * 1e-3) / 1e9
         result["decode"] = {"T": Td, "ms_per_step": round(dms, 4), "tokens_per_s": round(Td / (dms * 1e-3), 1),
                             "touched_experts": touched, "algorithmic_bytes": nbytes, "GB_per_s": round(gbs, 1),
-                            "pct_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
+                            "pct_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 2), "step_ms": dstats,
+                            "copy_GB_per_s": round(copy, 1),
                             "kernels_ms_per_step": {k: round(v["ms_per_step"], 4) for k, v in dkt.items()}}
         print("[bench] decode %.3f ms/step, %.0f GB/s" % (dms, gbs), file=sys.stderr, flush=True)
 

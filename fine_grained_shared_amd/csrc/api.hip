@@ -98,7 +98,7 @@ Layout layout_of(const moe_shape* s) {
     L.row_token = take(R * 4);
     L.pair_row = take(R * 4);
     L.chunks = take(nchunk * s->N_r * 4);
-    L.tiles = take(((size_t)s->N_r + 1) * 4);
+    L.tiles = take(moe::kTilePlans * ((size_t)s->N_r + 1) * 4);
     L.act = take(R * s->I * E);
     L.y_perm = take(R * s->H * E);
     L.act_sh = take(T * s->Ks * s->I * E);
@@ -161,6 +161,7 @@ int do_expert_ffn(const moe_shape* s, const void* x, const int32_t* row_token, c
     up.up_off = s->I;
     up.offsets = offsets;
     up.tiles = tiles;
+    up.tiles32 = tiles + (s->N_r + 1);
     up.G = s->N_r;
     up.max_rows = (int)R;
     up.C = act;
@@ -182,6 +183,7 @@ int do_expert_ffn(const moe_shape* s, const void* x, const int32_t* row_token, c
     dn.N = s->H;
     dn.offsets = offsets;
     dn.tiles = tiles;
+    dn.tiles32 = tiles + (s->N_r + 1);
     dn.G = s->N_r;
     dn.max_rows = (int)R;
     dn.C = y;

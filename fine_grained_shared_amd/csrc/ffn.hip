@@ -56,22 +56,17 @@ static int device_cus() {
 }
 
 // ---------------------------------------------------------------- tile plan
-// tiles[g] = sum_{g' < g} ceil(rows(g') / bm); tiles[G] = total m-tiles.  One workgroup, G <= 1024.
-__global__ __launch_bounds__(1024) void k_tile_plan(const int32_t* __restrict__ offsets, int G, int bm,
-                                                    int32_t* __restrict__ tiles) {
-    __shared__ int32_t wsum[16];
+// Exclusive prefix over g < G of v (one value per thread of the single 1024-thread workgroup);
+// out[G] = total.
+__device__ __forceinline__ void block_prefix(int v, int G, int32_t* __restrict__ out, int32_t* wsum) {
     const int g = threadIdx.x, lane = g & 63, w = g >> 6;
-    int v = 0;
-    if (g < G) {
-        const int rows = offsets[g + 1] - offsets[g];
-        v = rows > 0 ? (rows + bm - 1) / bm : 0;
-    }
     int incl = v;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
         const int x = __shfl_up(incl, o);
         if (lane >= o) incl += x;
     }
+    __syncthreads();   // wsum may still be read by a previous call
     if (lane == 63) wsum[w] = incl;
     __syncthreads();
     if (g == 0) {
@@ -81,10 +76,21 @@ __global__ __launch_bounds__(1024) void k_tile_plan(const int32_t* __restrict__ 
             wsum[q] = acc;
             acc += x;
         }
-        tiles[G] = acc;
+        out[G] = acc;
     }
     __syncthreads();
-    if (g < G) tiles[g] = wsum[w] + incl - v;
+    if (g < G) out[g] = wsum[w] + incl - v;
+}
+
+// tiles[g] = sum_{g' < g} ceil(rows(g') / bm), tiles[G] = total; then the same prefix for 32-row
+// tiles at tiles + G + 1.  One workgroup, G <= 1024.
+__global__ __launch_bounds__(1024) void k_tile_plan(const int32_t* __restrict__ offsets, int G, int bm,
+                                                    int32_t* __restrict__ tiles) {
+    __shared__ int32_t wsum[16];
+    const int g = threadIdx.x;
+    const int rows = g < G ? offsets[g + 1] - offsets[g] : 0;
+    block_prefix(rows > 0 ? (rows + bm - 1) / bm : 0, G, tiles, wsum);
+    block_prefix(rows > 0 ? (rows + 31) / 32 : 0, G, tiles + G + 1, wsum);
 }
 
 hipError_t launch_tile_plan(const int32_t* offsets, int G, int bm, int32_t* tiles, hipStream_t s) {
@@ -601,11 +607,18 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16_wide8(GemmParams p, int NT
     }
 }
 
+// s_waitcnt immediate (gfx9 layout): vmcnt in bits 3:0 and 15:14, expcnt 6:4 (not waited for here),
+// lgkmcnt 11:8.
+constexpr unsigned waitcnt_imm(int vm, int lgkm) {
+    return (unsigned)(vm & 15) | ((unsigned)((vm >> 4) & 3) << 14) | (7u << 4) | ((unsigned)(lgkm & 15) << 8);
+}
+static_assert(waitcnt_imm(63, 0) == 0xC07F, "vmcnt field layout");
+
 // LDS hand-off without waiting for outstanding global loads: LDS-op wait plus workgroup barrier.
 // The empty asm statements keep the compiler from moving LDS accesses across it.
 __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt not waited for
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));   // lgkmcnt(0); vmcnt and expcnt not waited for
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
 }
@@ -851,6 +864,153 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_w4(GemmParams p, int NT) {
     }
 }
 
+// ---------------------------------------------------------------- decode-shaped grouped GEMM
+// Few rows per group (decode: a handful of tokens per expert) make the expert GEMMs a stream of
+// weight bytes.  Tiles of 32 rows x 256 weight rows x 64 k; four waves, each 32 rows x 64 weight
+// rows (two 32 x 32 blocks; SwiGLU: 32 gate rows and the 32 matching up rows).  Operands go
+// straight to LDS (global_load_lds_dwordx4) through a ring of four 36 KB stages with three k-tiles
+// in flight, one workgroup per CU: about 108 KB of loads in flight per CU, which is what keeps
+// HBM busy here.  Each k-step: wait for this wave's loads of the k-tile (vmcnt), barrier, issue the
+// loads of k-tile kt+3 into the stage k-step kt-1 used, then 8 MFMAs per wave.
+constexpr int DBM = 32, DBN = 256, DSTAGES = 4;
+constexpr int kDTileA = DBM * BK * 2;            // 4 KB
+constexpr int kDStage = kDTileA + DBN * BK * 2;  // 36 KB
+constexpr int kDSmem = DSTAGES * kDStage;        // 144 KB
+constexpr int DEPW = DBN + 4;                    // fp32 staging row of the epilogue
+static_assert(DBM * DEPW * 4 <= kDSmem, "decode epilogue staging must fit");
+
+template <int MODE>
+__device__ __forceinline__ void gemm_tile_dec(const GemmParams& p, const TileInfo& ti, unsigned char* smem) {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, w = tid >> 6;   // w < 4
+    const uint16_t* A = (const uint16_t*)p.A;
+    const uint16_t* Bg = (const uint16_t*)p.B + (size_t)ti.g * p.sB_group;
+    // chunk permutation of a lane (chunk c of LDS row r holds global chunk c ^ ((r >> 1) & 7))
+    const int kcg0 = ((lane & 7) ^ ((lane >> 4) & 7)) * 8;
+    const int kcg1 = ((lane & 7) ^ ((4 + (lane >> 4)) & 7)) * 8;
+    // A chunk w: tile rows 8 w .. 8 w + 7
+    const uint16_t* ag;
+    {
+        const int r = min(8 * w + (lane >> 3), ti.rows - 1);
+        long long src = ti.row0 + r;
+        if (p.a_rows) src = min(max((long long)p.a_rows[src], 0LL), p.a_nrows - 1);
+        ag = A + src * p.lda + ((w & 1) ? kcg1 : kcg0);
+    }
+    // B chunks 8 w + i: tile rows 64 w + 8 i .. + 7
+    const uint16_t* bg[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        int wr;
+        if (MODE == GM_UP_SWIGLU) {
+            const int t = 32 * w + 8 * (i & 3) + (lane >> 3);
+            const int n = min(ti.nt * (DBN / 2) + t, p.N - 1);
+            wr = i < 4 ? n : p.up_off + n;
+        } else {
+            wr = min(ti.nt * DBN + 64 * w + 8 * i + (lane >> 3), p.N - 1);
+        }
+        bg[i] = Bg + (size_t)wr * p.ldb + ((i & 1) ? kcg1 : kcg0);
+    }
+    const int nk = p.K / BK;
+    auto issue = [&](int kt) {   // k-tile min(kt, nk - 1) into its stage
+        const int k = (kt < nk ? kt : nk - 1) * BK;
+        const int seg = k / p.Kseg;
+        const long long bo = (long long)seg * p.sB_seg + (k - seg * p.Kseg);
+        unsigned char* st = smem + (kt % DSTAGES) * kDStage;
+        dma16(ag + k, st + w * 1024);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) dma16(bg[i] + bo, st + kDTileA + (8 * w + i) * 1024);
+    };
+
+    f32x16 acc0, acc1;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+        acc0[q] = 0.f;
+        acc1[q] = 0.f;
+    }
+    __syncthreads();   // the previous tile's epilogue may still read the LDS staging area
+    issue(0);
+    issue(1);
+    issue(2);
+    for (int kt = 0; kt < nk; ++kt) {
+        // this wave's loads of k-tile kt have landed once at most the two newer k-tiles (9 loads
+        // each) are outstanding; the barrier then covers every wave's loads and every wave's reads
+        // of the stage k-step kt-1 used, which the next issue overwrites
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(18, 0));
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        issue(kt + 3);
+        const unsigned char* sa = smem + (kt % DSTAGES) * kDStage;
+        const unsigned char* sb = sa + kDTileA;
+#pragma unroll
+        for (int s = 0; s < BK / 16; ++s) {
+            const int kc = 2 * s + (lane >> 5);
+            const bf16x8 a = frag(sa, lane & 31, kc);
+            const bf16x8 b0 = frag(sb, 64 * w + (lane & 31), kc);
+            const bf16x8 b1 = frag(sb, 64 * w + 32 + (lane & 31), kc);
+            acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b0, acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b1, acc1, 0, 0, 0);
+        }
+    }
+    // drain the trailing (clamped) loads before the LDS is reused for staging
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    // ---- epilogue: stage the 32 x 256 (SwiGLU: 32 x 128) fp32 tile, then 8-column row pieces
+    float* st = reinterpret_cast<float*>(smem);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+        const int rl = 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+        if (MODE == GM_UP_SWIGLU) {
+            st[rl * DEPW + 32 * w + (lane & 31)] = silu(acc0[q]) * acc1[q];
+        } else {
+            st[rl * DEPW + 64 * w + (lane & 31)] = acc0[q];
+            st[rl * DEPW + 64 * w + 32 + (lane & 31)] = acc1[q];
+        }
+    }
+    __syncthreads();
+    constexpr int OUTW = MODE == GM_UP_SWIGLU ? DBN / 2 : DBN;
+    constexpr int TPR = OUTW / 8;    // threads per row
+    constexpr int RPP = 256 / TPR;   // rows per pass
+    const int cq = (tid % TPR) * 8;
+    const int col0 = ti.nt * OUTW + cq;
+    if (col0 >= p.N) return;
+    for (int rl = tid / TPR; rl < ti.rows; rl += RPP) {
+        const float4 v0 = *reinterpret_cast<const float4*>(&st[rl * DEPW + cq]);
+        const float4 v1 = *reinterpret_cast<const float4*>(&st[rl * DEPW + cq + 4]);
+        float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+        epilogue_row<MODE>(p, ti, v, rl, col0);
+    }
+}
+
+template <int MODE>
+__global__ __launch_bounds__(256, 1) void k_gemm_bf16_dec(GemmParams p, int NT) {
+    __shared__ __attribute__((aligned(16))) unsigned char smem[kDSmem];
+    const int total = p.tiles32[p.G] * NT;
+    const int xcd = blockIdx.x & 7, loc = blockIdx.x >> 3, per_xcd = gridDim.x >> 3;
+    const int beg = (int)((long long)total * xcd / 8);
+    const int end = (int)((long long)total * (xcd + 1) / 8);
+    for (int L = beg + loc; L < end; L += per_xcd) {
+        // decode L over the 32-row tile prefix
+        const int mt = L / NT;
+        int lo = 0, hi = p.G;
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (p.tiles32[mid] <= mt) lo = mid;
+            else hi = mid;
+        }
+        TileInfo ti;
+        const int t0 = p.tiles32[lo], nm = p.tiles32[lo + 1] - t0;
+        int ml;
+        blocked_mn(L - t0 * NT, nm, NT, ml, ti.nt);
+        ti.g = lo;
+        ti.row0 = p.offsets[lo] + ml * DBM;
+        ti.rows = min(DBM, p.offsets[lo + 1] - ti.row0);
+        gemm_tile_dec<MODE>(p, ti, smem);
+    }
+}
+
 __device__ __forceinline__ int wide_nt(const GemmParams& p, int mode) {
     return mode == GM_UP_SWIGLU ? (p.N + 255) / 256 : (p.N + WBN - 1) / WBN;
 }
@@ -977,6 +1137,19 @@ hipError_t launch_gemm(int dtype, int mode, const GemmParams& p_in, hipStream_t 
         else if (mode == GM_UP_RELU) MOE_LAUNCH_W(GM_UP_RELU);
         else MOE_LAUNCH_W(GM_DOWN);
 #undef MOE_LAUNCH_W
+        return hipGetLastError();
+    }
+    if (p.offsets && p.tiles32 && rows_per_group < 64 &&
+        (mode == GM_UP_SWIGLU || mode == GM_UP_RELU || mode == GM_DOWN)) {
+        // decode-shaped: 32-row tiles, deep load pipeline, one workgroup per CU
+        const int NTd = mode == GM_UP_SWIGLU ? (p.N + DBN / 2 - 1) / (DBN / 2) : (p.N + DBN - 1) / DBN;
+        const long long mtd = (p.max_rows + DBM - 1) / DBM + p.G;   // upper bound of the 32-row m-tiles
+        long long nb = (mtd * NTd + 7) / 8 * 8;
+        nb = nb < cus ? nb : cus;
+        const dim3 grid((unsigned)((nb + 7) / 8 * 8));
+        if (mode == GM_UP_SWIGLU) hipLaunchKernelGGL(k_gemm_bf16_dec<GM_UP_SWIGLU>, grid, dim3(256), 0, s, p, NTd);
+        else if (mode == GM_UP_RELU) hipLaunchKernelGGL(k_gemm_bf16_dec<GM_UP_RELU>, grid, dim3(256), 0, s, p, NTd);
+        else hipLaunchKernelGGL(k_gemm_bf16_dec<GM_DOWN>, grid, dim3(256), 0, s, p, NTd);
         return hipGetLastError();
     }
     const int NT = mode == GM_UP_SWIGLU ? (p.N + 63) / 64 : (p.N + BN - 1) / BN;

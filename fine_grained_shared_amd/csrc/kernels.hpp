@@ -52,6 +52,7 @@ struct GemmParams {
     int up_off;               // SwiGLU: first up row inside a group's w1 (= I)
     const int32_t* offsets;   // grouped mode: [G+1] row-space segments (NULL: dense mode)
     const int32_t* tiles;     // grouped mode: [G+1] prefix of m-tiles per group
+    const int32_t* tiles32;   // grouped mode: [G+1] prefix of 32-row m-tiles per group (decode kernel)
     int M_dense;              // dense mode: every group covers rows [0, M_dense)
     int G;
     int max_rows;             // upper bound of the row space (grid sizing)
@@ -72,7 +73,9 @@ struct GemmParams {
     int a_bytes;
     int b_bytes;
 };
-// m-tile prefix of the groups defined by offsets (grouped mode), for tiles of bm rows
+// m-tile prefixes of the groups defined by offsets (grouped mode): tiles[0..G] for tiles of bm rows,
+// tiles[G+1 .. 2G+1] for tiles of 32 rows.
+constexpr int kTilePlans = 2;
 hipError_t launch_tile_plan(const int32_t* offsets, int G, int bm, int32_t* tiles, hipStream_t s);
 int gemm_bm(int dtype);
 hipError_t launch_gemm(int dtype, int mode, const GemmParams& p, hipStream_t s);
