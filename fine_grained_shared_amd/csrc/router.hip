@@ -57,6 +57,60 @@ __global__ __launch_bounds__(256) void k_logits_bf16(const uint16_t* __restrict_
     }
 }
 
+// ---------------------------------------------------------------- logits, bf16, few tokens
+// Decode-sized T: a workgroup computes 16 tokens x 16 experts; its four waves take contiguous
+// quarters of H and keep eight 32-wide k-chunks of loads in flight (latency, not bandwidth, bounds
+// this shape), then the four partial sums are added in a fixed order through LDS.
+__global__ __launch_bounds__(256) void k_logits_bf16_sk(const uint16_t* __restrict__ u,
+                                                        const uint16_t* __restrict__ e,
+                                                        float* __restrict__ logits, int T, int H, int N) {
+    __shared__ f32x4 part[4][64];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int r = lane & 15, kq = (lane >> 4) * 8;
+    const int t = min((int)blockIdx.x * 16 + r, T - 1);
+    const int ex = min((int)blockIdx.y * 16 + r, N - 1);
+    const uint16_t* ap = u + (size_t)t * H + kq;
+    const uint16_t* bp = e + (size_t)ex * H + kq;
+    const int nch = H / 32;
+    const int c0 = nch * w / 4, c1 = nch * (w + 1) / 4;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    int c = c0;
+    for (; c + 8 <= c1; c += 8) {
+        uint4 av[8], bv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            av[j] = *reinterpret_cast<const uint4*>(ap + (c + j) * 32);
+            bv[j] = *reinterpret_cast<const uint4*>(bp + (c + j) * 32);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[j]),
+                                                          __builtin_bit_cast(bf16x8, bv[j]), acc, 0, 0, 0);
+    }
+    for (; c < c1; ++c) {
+        const uint4 av = *reinterpret_cast<const uint4*>(ap + c * 32);
+        const uint4 bv = *reinterpret_cast<const uint4*>(bp + c * 32);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, bv),
+                                                      acc, 0, 0, 0);
+    }
+    part[w][lane] = acc;
+    __syncthreads();
+    if (w == 0) {
+        f32x4 v = part[0][lane];
+#pragma unroll
+        for (int q = 1; q < 4; ++q) v += part[q][lane];
+        // D[i][j]: j = lane % 16 (expert), i = 4 * (lane / 16) + q (token)
+        const int col = blockIdx.y * 16 + r;
+        if (col < N) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int tt = blockIdx.x * 16 + (lane >> 4) * 4 + q;
+                if (tt < T) logits[(size_t)tt * N + col] = v[q];
+            }
+        }
+    }
+}
+
 // ---------------------------------------------------------------- logits, fp32 (VALU)
 __global__ __launch_bounds__(256) void k_logits_f32(const float* __restrict__ u, const float* __restrict__ e,
                                                     float* __restrict__ logits, int T, int H, int N) {
@@ -94,6 +148,12 @@ hipError_t launch_logits(int dtype, const void* u, const void* e, float* logits,
         p.C = logits;
         p.ldc = N;
         return launch_gemm(1, GM_F32OUT, p, s);
+    } else if (T < 1024) {
+        // one kernel (one summation order) for every T below the GEMM path, so a token's logits do
+        // not depend on how the tokens are batched
+        dim3 grid((T + 15) / 16, (N + 15) / 16);
+        hipLaunchKernelGGL(k_logits_bf16_sk, grid, dim3(256), 0, s, (const uint16_t*)u, (const uint16_t*)e,
+                           logits, T, H, N);
     } else if (T >= 2048) {
         dim3 grid((T + 63) / 64, (N + 63) / 64);
         hipLaunchKernelGGL(k_logits_bf16<4>, grid, dim3(256), 0, s, (const uint16_t*)u, (const uint16_t*)e,
