@@ -984,29 +984,40 @@ __device__ __forceinline__ void gemm_tile_dec(const GemmParams& p, const TileInf
     }
 }
 
-template <int MODE>
+// Grouped: tiles over the 32-row tile prefix; dense (a few tokens through the shared experts): every
+// group covers rows [0, M_dense) in 32-row tiles.
+template <int MODE, bool GROUPED>
 __global__ __launch_bounds__(256, 1) void k_gemm_bf16_dec(GemmParams p, int NT) {
+    if (GROUPED != (p.offsets != nullptr)) return;  // launched with the matching instantiation only
     __shared__ __attribute__((aligned(16))) unsigned char smem[kDSmem];
-    const int total = p.tiles32[p.G] * NT;
+    const int nmd = (p.M_dense + DBM - 1) / DBM;     // dense: m-tiles per group
+    const int total = GROUPED ? p.tiles32[p.G] * NT : p.G * nmd * NT;
     const int xcd = blockIdx.x & 7, loc = blockIdx.x >> 3, per_xcd = gridDim.x >> 3;
     const int beg = (int)((long long)total * xcd / 8);
     const int end = (int)((long long)total * (xcd + 1) / 8);
     for (int L = beg + loc; L < end; L += per_xcd) {
-        // decode L over the 32-row tile prefix
-        const int mt = L / NT;
-        int lo = 0, hi = p.G;
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (p.tiles32[mid] <= mt) lo = mid;
-            else hi = mid;
-        }
         TileInfo ti;
-        const int t0 = p.tiles32[lo], nm = p.tiles32[lo + 1] - t0;
         int ml;
-        blocked_mn(L - t0 * NT, nm, NT, ml, ti.nt);
-        ti.g = lo;
-        ti.row0 = p.offsets[lo] + ml * DBM;
-        ti.rows = min(DBM, p.offsets[lo + 1] - ti.row0);
+        if (GROUPED) {
+            const int mt = L / NT;
+            int lo = 0, hi = p.G;
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (p.tiles32[mid] <= mt) lo = mid;
+                else hi = mid;
+            }
+            const int t0 = p.tiles32[lo], nm = p.tiles32[lo + 1] - t0;
+            blocked_mn(L - t0 * NT, nm, NT, ml, ti.nt);
+            ti.g = lo;
+            ti.row0 = p.offsets[lo] + ml * DBM;
+            ti.rows = min(DBM, p.offsets[lo + 1] - ti.row0);
+        } else {
+            const int per = nmd * NT;
+            ti.g = L / per;
+            blocked_mn(L - ti.g * per, nmd, NT, ml, ti.nt);
+            ti.row0 = ml * DBM;
+            ti.rows = min(DBM, p.M_dense - ti.row0);
+        }
         gemm_tile_dec<MODE>(p, ti, smem);
     }
 }
@@ -1139,17 +1150,30 @@ hipError_t launch_gemm(int dtype, int mode, const GemmParams& p_in, hipStream_t 
 #undef MOE_LAUNCH_W
         return hipGetLastError();
     }
-    if (p.offsets && p.tiles32 && rows_per_group < 64 &&
-        (mode == GM_UP_SWIGLU || mode == GM_UP_RELU || mode == GM_DOWN)) {
-        // decode-shaped: 32-row tiles, deep load pipeline, one workgroup per CU
+    // decode-shaped: 32-row tiles, deep load pipeline, one workgroup per CU.  Grouped problems with few
+    // rows per group, and dense ones with few rows (the shared experts of a decode step, including the
+    // fused combine).  Every GEMM kernel here accumulates an output in the same order (one fp32 MFMA
+    // chain over ascending 16-deep k-chunks), so the choice does not change any result bit.
+    const bool dec_grouped = p.offsets && p.tiles32 && rows_per_group < 64 &&
+                             (mode == GM_UP_SWIGLU || mode == GM_UP_RELU || mode == GM_DOWN);
+    const bool dec_dense = !p.offsets && p.M_dense < 512 && mode != GM_F32OUT;
+    if (dec_grouped || dec_dense) {
         const int NTd = mode == GM_UP_SWIGLU ? (p.N + DBN / 2 - 1) / (DBN / 2) : (p.N + DBN - 1) / DBN;
-        const long long mtd = (p.max_rows + DBM - 1) / DBM + p.G;   // upper bound of the 32-row m-tiles
+        const long long mtd = p.offsets ? (p.max_rows + DBM - 1) / DBM + p.G   // upper bound of the m-tiles
+                                        : (long long)p.G * ((p.M_dense + DBM - 1) / DBM);
         long long nb = (mtd * NTd + 7) / 8 * 8;
         nb = nb < cus ? nb : cus;
         const dim3 grid((unsigned)((nb + 7) / 8 * 8));
-        if (mode == GM_UP_SWIGLU) hipLaunchKernelGGL(k_gemm_bf16_dec<GM_UP_SWIGLU>, grid, dim3(256), 0, s, p, NTd);
-        else if (mode == GM_UP_RELU) hipLaunchKernelGGL(k_gemm_bf16_dec<GM_UP_RELU>, grid, dim3(256), 0, s, p, NTd);
-        else hipLaunchKernelGGL(k_gemm_bf16_dec<GM_DOWN>, grid, dim3(256), 0, s, p, NTd);
+#define MOE_LAUNCH_D(M)                                                                          \
+    do {                                                                                         \
+        if (p.offsets) hipLaunchKernelGGL((k_gemm_bf16_dec<M, true>), grid, dim3(256), 0, s, p, NTd); \
+        else hipLaunchKernelGGL((k_gemm_bf16_dec<M, false>), grid, dim3(256), 0, s, p, NTd);    \
+    } while (0)
+        if (mode == GM_UP_SWIGLU) MOE_LAUNCH_D(GM_UP_SWIGLU);
+        else if (mode == GM_UP_RELU) MOE_LAUNCH_D(GM_UP_RELU);
+        else if (mode == GM_DOWN) MOE_LAUNCH_D(GM_DOWN);
+        else hipLaunchKernelGGL((k_gemm_bf16_dec<GM_DOWN_COMBINE, false>), grid, dim3(256), 0, s, p, NTd);
+#undef MOE_LAUNCH_D
         return hipGetLastError();
     }
     const int NT = mode == GM_UP_SWIGLU ? (p.N + 63) / 64 : (p.N + BN - 1) / BN;
