@@ -24,7 +24,13 @@ if ROOT not in sys.path:
 import numpy as np
 
 METRIC = "MoE-layer tokens/s and TFLOP/s (% bf16 MFMA peak) at V3-style shape; decode HBM GB/s"
-DOMINANT_KERNEL = "k_gemm_bf16_w4<0, true>"   # routed gate/up grouped GEMM + SwiGLU
+# routed gate/up grouped GEMM + SwiGLU: [out, in] banks, and banks in fragment order (moe_pack_weights)
+DOMINANT_KERNELS = ("k_gemm_bf16_w4<0, true>", "k_gemm_bf16_w4p<0, false>")
+
+
+def dominant_kernel(flags):
+    return DOMINANT_KERNELS[1] if flags else DOMINANT_KERNELS[0]
+
 KERNEL_SOURCES = ["fine_grained_shared_amd/csrc/ffn.hip", "fine_grained_shared_amd/csrc/kernels.hpp",
                   "fine_grained_shared_amd/csrc/common.hpp"]
 TRAFFIC_FILE = "profiles/traffic_ffn_up_v3_prefill.json"
@@ -78,15 +84,15 @@ def kernel_source_hash():
     return h.hexdigest()
 
 
-def measured_traffic():
+def measured_traffic(kernel):
     """HBM bytes per launch of the dominant kernel from the committed counter summary, or None
-    when the kernel sources changed since the counters were taken."""
+    when the kernel sources changed since the counters were taken or they cover another kernel."""
     path = os.path.join(ROOT, TRAFFIC_FILE)
     if not os.path.exists(path):
         return None
     with open(path) as fh:
         t = json.load(fh)
-    if t.get("source_sha256") != kernel_source_hash():
+    if t.get("source_sha256") != kernel_source_hash() or t.get("dominant_kernel") != kernel:
         return None
     return t.get("traffic_bytes_per_launch")
 
@@ -115,6 +121,7 @@ def rocprof_summary(trace_dir, fetch_dir=None, write_dir=None, out_json=None):
     lines = []
     stats = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)
     dom = None
+    dom_name = DOMINANT_KERNELS[0]
     for f in stats:
         with open(f) as fh:
             rows = list(csv.DictReader(fh))
@@ -125,9 +132,10 @@ def rocprof_summary(trace_dir, fetch_dir=None, write_dir=None, out_json=None):
             avg = float(r["AverageNs"]) / 1e6
             lines.append("| %s | %s | %.4f | %.3f | %.1f |" % (nm, r["Calls"], avg, float(r["TotalDurationNs"]) / 1e6,
                                                               float(r["Percentage"])))
-            if nm.endswith(DOMINANT_KERNEL):
-                dom = avg
-    res = {"dominant_kernel": DOMINANT_KERNEL, "avg_ms": dom}
+            for cand in DOMINANT_KERNELS:
+                if nm.endswith(cand):
+                    dom, dom_name = avg, cand
+    res = {"dominant_kernel": dom_name, "avg_ms": dom}
     if fetch_dir and write_dir:
         fc, wc = _read_counters(fetch_dir), _read_counters(write_dir)
 
@@ -142,8 +150,8 @@ def rocprof_summary(trace_dir, fetch_dir=None, write_dir=None, out_json=None):
             return max(vals) if vals else None
         copy_f = copy_ref(fc, "FETCH_SIZE")
         copy_w = copy_ref(wc, "WRITE_SIZE")
-        k_f = pick(fc, DOMINANT_KERNEL, "FETCH_SIZE")
-        k_w = pick(wc, DOMINANT_KERNEL, "WRITE_SIZE")
+        k_f = pick(fc, dom_name, "FETCH_SIZE")
+        k_w = pick(wc, dom_name, "WRITE_SIZE")
         if None not in (copy_f, copy_w, k_f, k_w):
             sf, sw = COPY_BYTES / (copy_f * 1024), COPY_BYTES / (copy_w * 1024)
             res.update({"copy_fetch_kib": copy_f, "copy_write_kib": copy_w, "fetch_kib_per_launch": k_f,
@@ -153,7 +161,7 @@ def rocprof_summary(trace_dir, fetch_dir=None, write_dir=None, out_json=None):
             lines.append("")
             lines.append("HBM traffic of %s per launch: FETCH_SIZE %.0f KiB x %.3f + WRITE_SIZE %.0f KiB x %.3f "
                          "= %.3f GB (scales: a plain %d-byte device copy reads FETCH %.0f KiB / WRITE %.0f KiB)" % (
-                             DOMINANT_KERNEL, k_f, sf, k_w, sw, res["traffic_bytes_per_launch"] / 1e9, COPY_BYTES,
+                             dom_name, k_f, sf, k_w, sw, res["traffic_bytes_per_launch"] / 1e9, COPY_BYTES,
                              copy_f, copy_w))
     if out_json:
         with open(out_json, "w") as fh:
@@ -289,6 +297,9 @@ def main():
     ap.add_argument("--pmc-fetch", metavar="DIR")
     ap.add_argument("--pmc-write", metavar="DIR")
     ap.add_argument("--traffic-json", metavar="FILE")
+    ap.add_argument("--weights", choices=("packed", "unpacked"), default="unpacked",
+                    help="routed expert banks in fragment order (moe_pack_weights, done once before timing) "
+                         "or in the [out, in] layout")
     args = ap.parse_args()
     if args.rocprof_summary:
         text, _ = rocprof_summary(args.rocprof_summary, args.pmc_fetch, args.pmc_write, args.traffic_json)
@@ -310,8 +321,15 @@ def main():
     inp = synth.make_inputs(w)
     gen_s = time.time() - t0
     d = _upload(inp)
+    flags = 0
+    if args.weights == "packed":
+        # a storage layout of the same weights, made once when they are loaded (not part of a step)
+        for k in ("w1", "w2"):
+            d[k] = moe.pack_weights(d[k])
+        flags = moe.MOE_FLAG_PACKED_WEIGHTS
     torch.cuda.synchronize()
-    print("[bench] inputs generated in %.1f s and uploaded" % gen_s, file=sys.stderr, flush=True)
+    print("[bench] inputs generated in %.1f s and uploaded (%s routed banks)" % (gen_s, args.weights),
+          file=sys.stderr, flush=True)
 
     # plain 1 GiB device copy: reference point for the HBM byte counters of a profiled run
     src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
@@ -327,7 +345,7 @@ def main():
 
     def step():
         moe.moe_layer_forward(shape, d["u"], d["centroids"], d["bias"], d["w1"], d["b1"], d["w2"], d["w1_sh"],
-                              d["b1_sh"], d["w2_sh"], 0, out, idx, wts, ws)
+                              d["b1_sh"], d["w2_sh"], flags, out, idx, wts, ws)
 
     ms = _time_steps(step, args.steps, args.warmup)
     print("[bench] prefill %.3f ms/step" % ms, file=sys.stderr, flush=True)
@@ -355,13 +373,14 @@ def main():
         "data": "synthetic (seeded N(0,1) tokens, N(0,1/fan_in) weights, N(0,1/H) centroids, bias N(0,0.01))",
         "config": {"workload": w.desc, "T": w.T, "H": w.H, "N_r": w.N_r, "K_r": w.K_r, "Ks": w.Ks, "I": w.I,
                    "gating": "sigmoid+selection bias, normalised over selected",
-                   "act": "SwiGLU", "parallelism": "single GPU"},
+                   "act": "SwiGLU", "parallelism": "single GPU",
+                   "routed_weights": "fragment order (packed once at load)" if flags else "[out, in]"},
         "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
         "pct_bf16_peak": round(100 * flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
-        "roofline": {"kernel": "routed expert gate/up grouped GEMM + SwiGLU (%s)" % DOMINANT_KERNEL,
+        "roofline": {"kernel": "routed expert gate/up grouped GEMM + SwiGLU (%s)" % dominant_kernel(flags),
                      "bound": "mfma", "achieved": round(up_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(up_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": measured_traffic(),
+                     "traffic": measured_traffic(dominant_kernel(flags)),
                      "avg_launch_ms": round(up_ms, 4),
                      "algorithmic_flops_per_launch": routed_up_flops(w)},
         "kernels_ms_per_step": {k: round(v["ms_per_step"], 4) for k, v in kt.items()},
@@ -381,7 +400,7 @@ def main():
 
         def dstep():
             moe.moe_layer_forward(sd, ud, d["centroids"], d["bias"], d["w1"], d["b1"], d["w2"], d["w1_sh"],
-                                  d["b1_sh"], d["w2_sh"], 0, outd, idxd, wtd, wsd)
+                                  d["b1_sh"], d["w2_sh"], flags, outd, idxd, wtd, wsd)
 
         dms = _time_steps(dstep, max(args.steps, 10), args.warmup)
         dstats = _step_stats(dstep, max(args.steps, 10))

@@ -23,14 +23,15 @@ MOE_GATE_SOFTMAX, MOE_GATE_SIGMOID_BIAS_NORM, MOE_GATE_SOFTMAX_RENORM = 0, 1, 2
 MOE_ACT_RELU_BIAS, MOE_ACT_SWIGLU = 0, 1
 MOE_F32, MOE_BF16 = 0, 1
 MOE_FLAG_NO_RESIDUAL = 1
+MOE_FLAG_PACKED_WEIGHTS = 2
 (MOE_PROF_ROUTER, MOE_PROF_DISPATCH, MOE_PROF_FFN_UP, MOE_PROF_FFN_DOWN, MOE_PROF_SHARED_UP,
  MOE_PROF_SHARED_DOWN, MOE_PROF_COMBINE, MOE_PROF_OTHER) = range(8)
 PROF_NAMES = ["router", "dispatch", "ffn_up", "ffn_down", "shared_up", "shared_down", "combine", "other"]
 
 # every entry point of include/moe.h
-EXPORTS = ("moe_workspace_size", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_shared_ffn",
-           "moe_combine", "moe_layer_forward", "moe_bias_update", "moe_status_string",
-           "moe_last_hip_error", "moe_profile_enable", "moe_profile_query")
+EXPORTS = ("moe_workspace_size", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_pack_weights",
+           "moe_expert_ffn_packed", "moe_shared_ffn", "moe_combine", "moe_layer_forward", "moe_bias_update",
+           "moe_status_string", "moe_last_hip_error", "moe_profile_enable", "moe_profile_query")
 
 
 class MoeShape(ctypes.Structure):
@@ -69,6 +70,8 @@ def load() -> ctypes.CDLL:
         "moe_route": [sp, vp, vp, vp, vp, vp, vp, sz, vp],
         "moe_dispatch": [sp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "moe_expert_ffn": [sp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+        "moe_pack_weights": [vp, vp, i32, i32, i32, vp],
+        "moe_expert_ffn_packed": [sp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "moe_shared_ffn": [sp, vp, vp, vp, vp, vp, vp, sz, vp],
         "moe_combine": [sp, vp, vp, vp, vp, vp, vp, vp],
         "moe_layer_forward": [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, sz, vp],
@@ -151,6 +154,17 @@ def moe_expert_ffn(shape, x, row_token, offsets, w1, b1, w2, y, ws, stream=None)
            "moe_expert_ffn")
 
 
+def moe_pack_weights(w, packed, G, N, K, stream=None):
+    _check(load().moe_pack_weights(_ptr(w), _ptr(packed), int(G), int(N), int(K), _stream(stream)),
+           "moe_pack_weights")
+
+
+def moe_expert_ffn_packed(shape, x, row_token, offsets, w1, b1, w2, y, ws, stream=None):
+    _check(load().moe_expert_ffn_packed(ctypes.byref(shape), _ptr(x), _ptr(row_token), _ptr(offsets), _ptr(w1),
+                                        _ptr(b1), _ptr(w2), _ptr(y), _ptr(ws), _nbytes(ws), _stream(stream)),
+           "moe_expert_ffn_packed")
+
+
 def moe_shared_ffn(shape, x, w1_sh, b1_sh, w2_sh, y, ws, stream=None):
     _check(load().moe_shared_ffn(ctypes.byref(shape), _ptr(x), _ptr(w1_sh), _ptr(b1_sh), _ptr(w2_sh), _ptr(y),
                                  _ptr(ws), _nbytes(ws), _stream(stream)), "moe_shared_ffn")
@@ -196,6 +210,15 @@ def workspace(shape: MoeShape, device="cuda"):
     import torch
     n = moe_workspace_size(shape)
     return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def pack_weights(w, stream=None):
+    """Return a new tensor holding the [G, N, K] bf16 bank w in the packed order of moe_pack_weights."""
+    import torch
+    G, N, K = w.shape
+    out = torch.empty_like(w, memory_format=torch.contiguous_format)
+    moe_pack_weights(w, out, G, N, K, stream)
+    return out
 
 
 def layer_forward(shape, u, centroids, bias, w1, b1, w2, w1_sh=None, b1_sh=None, w2_sh=None, flags=0,

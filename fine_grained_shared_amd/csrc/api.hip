@@ -76,6 +76,15 @@ int check_shape(const moe_shape* s) {
 
 size_t esz(const moe_shape* s) { return s->dtype == MOE_F32 ? 4 : 2; }
 
+// Routed banks in fragment order: bf16 only, and each expert's matrix addressed with 32-bit offsets.
+constexpr long long kPackedMatrixMaxBytes = 0x7FFFFFF0LL;
+int check_packed(const moe_shape* s) {
+    if (s->dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+    const long long n1 = s->act == MOE_ACT_SWIGLU ? 2LL * s->I : (long long)s->I;
+    if (n1 * s->H * 2 > kPackedMatrixMaxBytes) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
 // Workspace regions (byte offsets, each 256-byte aligned).
 struct Layout {
     size_t logits, topk_idx, topk_w, offsets, row_token, pair_row, chunks, tiles, act, y_perm, act_sh, y_sh, total;
@@ -140,7 +149,7 @@ int do_dispatch(const moe_shape* s, const int32_t* idx, int32_t* offsets, int32_
 
 int do_expert_ffn(const moe_shape* s, const void* x, const int32_t* row_token, const int32_t* offsets,
                   const void* w1, const float* b1, const void* w2, void* y, int32_t* tiles, void* act,
-                  hipStream_t st) {
+                  hipStream_t st, bool packed) {
     const long long R = (long long)s->T * s->K_r;
     if (R == 0 || s->N_r == 0) return MOE_OK;
     const int n1 = s->act == MOE_ACT_SWIGLU ? 2 * s->I : s->I;
@@ -168,6 +177,7 @@ int do_expert_ffn(const moe_shape* s, const void* x, const int32_t* row_token, c
     up.ldc = s->I;
     up.bias = b1;
     up.sbias_group = s->I;
+    up.packed = packed;
     const int up_mode = s->act == MOE_ACT_SWIGLU ? moe::GM_UP_SWIGLU : moe::GM_UP_RELU;
     MOE_TRY(MOE_PROF_FFN_UP, st, moe::launch_gemm(s->dtype, up_mode, up, st));
     moe::GemmParams dn{};
@@ -188,6 +198,7 @@ int do_expert_ffn(const moe_shape* s, const void* x, const int32_t* row_token, c
     dn.max_rows = (int)R;
     dn.C = y;
     dn.ldc = s->H;
+    dn.packed = packed;
     MOE_TRY(MOE_PROF_FFN_DOWN, st, moe::launch_gemm(s->dtype, moe::GM_DOWN, dn, st));
     return MOE_OK;
 }
@@ -299,9 +310,9 @@ int moe_dispatch(const moe_shape* s, const int32_t* topk_idx, int32_t* offsets, 
     return MOE_OK;
 }
 
-int moe_expert_ffn(const moe_shape* s, const void* x, const int32_t* row_token, const int32_t* offsets,
-                   const void* w1, const float* b1, const void* w2, void* y, void* ws, size_t ws_bytes,
-                   void* stream) {
+static int expert_ffn(const moe_shape* s, const void* x, const int32_t* row_token, const int32_t* offsets,
+                      const void* w1, const float* b1, const void* w2, void* y, void* ws, size_t ws_bytes,
+                      void* stream, bool packed) {
     int rc = check_shape(s);
     if (rc != MOE_OK) return rc;
     const long long R = (long long)s->T * s->K_r;
@@ -309,10 +320,36 @@ int moe_expert_ffn(const moe_shape* s, const void* x, const int32_t* row_token, 
     if (!x || !offsets || !w1 || !w2 || !y) return MOE_ERR_INVALID_ARG;
     if (!aligned16(x) || !aligned16(w1) || !aligned16(w2) || !aligned16(y)) return MOE_ERR_INVALID_ARG;
     if (b1 && s->act != MOE_ACT_RELU_BIAS) return MOE_ERR_INVALID_ARG;
+    if (packed && (rc = check_packed(s)) != MOE_OK) return rc;
     if ((rc = check_ws(s, ws, ws_bytes)) != MOE_OK) return rc;
     const Layout L = layout_of(s);
     return do_expert_ffn(s, x, row_token, offsets, w1, b1, w2, y, at<int32_t>(ws, L.tiles), at<void>(ws, L.act),
-                         (hipStream_t)stream);
+                         (hipStream_t)stream, packed);
+}
+
+int moe_expert_ffn(const moe_shape* s, const void* x, const int32_t* row_token, const int32_t* offsets,
+                   const void* w1, const float* b1, const void* w2, void* y, void* ws, size_t ws_bytes,
+                   void* stream) {
+    return expert_ffn(s, x, row_token, offsets, w1, b1, w2, y, ws, ws_bytes, stream, false);
+}
+
+int moe_expert_ffn_packed(const moe_shape* s, const void* x, const int32_t* row_token, const int32_t* offsets,
+                          const void* w1, const float* b1, const void* w2, void* y, void* ws, size_t ws_bytes,
+                          void* stream) {
+    return expert_ffn(s, x, row_token, offsets, w1, b1, w2, y, ws, ws_bytes, stream, true);
+}
+
+int moe_pack_weights(const void* w, void* packed, int32_t G, int32_t N, int32_t K, void* stream) {
+    if (G < 0 || N <= 0 || K <= 0 || N % 32 || K % 64) return MOE_ERR_INVALID_ARG;
+    if ((long long)N * K * 2 > kPackedMatrixMaxBytes) return MOE_ERR_UNSUPPORTED;
+    if (G == 0) return MOE_OK;
+    if (!w || !packed || !aligned16(w) || !aligned16(packed)) return MOE_ERR_INVALID_ARG;
+    const uintptr_t bytes = (uintptr_t)G * (uintptr_t)N * (uintptr_t)K * 2u;
+    const uintptr_t a = (uintptr_t)w, b = (uintptr_t)packed;
+    if (a < b + bytes && b < a + bytes) return MOE_ERR_INVALID_ARG;   // overlapping buffers
+    hipStream_t st = (hipStream_t)stream;
+    MOE_TRY(MOE_PROF_OTHER, st, moe::launch_pack_b(w, packed, G, N, K, st));
+    return MOE_OK;
 }
 
 int moe_shared_ffn(const moe_shape* s, const void* x, const void* w1_sh, const float* b1_sh, const void* w2_sh,
@@ -348,7 +385,9 @@ int moe_layer_forward(const moe_shape* s, const void* u, const void* centroids, 
                       void* stream) {
     int rc = check_shape(s);
     if (rc != MOE_OK) return rc;
-    if (flags & ~MOE_FLAG_NO_RESIDUAL) return MOE_ERR_INVALID_ARG;
+    if (flags & ~(MOE_FLAG_NO_RESIDUAL | MOE_FLAG_PACKED_WEIGHTS)) return MOE_ERR_INVALID_ARG;
+    const bool packed = (flags & MOE_FLAG_PACKED_WEIGHTS) != 0;
+    if (packed && (rc = check_packed(s)) != MOE_OK) return rc;
     if (bias && s->gating != MOE_GATE_SIGMOID_BIAS_NORM) return MOE_ERR_INVALID_ARG;
     if ((b1 || b1_sh) && s->act != MOE_ACT_RELU_BIAS) return MOE_ERR_INVALID_ARG;
     if (s->T == 0) return MOE_OK;
@@ -371,7 +410,7 @@ int moe_layer_forward(const moe_shape* s, const void* u, const void* centroids, 
                               st)) != MOE_OK)
             return rc;
         if ((rc = do_expert_ffn(s, u, at<int32_t>(ws, L.row_token), offsets, w1, b1, w2, y_perm,
-                                at<int32_t>(ws, L.tiles), at<void>(ws, L.act), st)) != MOE_OK)
+                                at<int32_t>(ws, L.tiles), at<void>(ws, L.act), st, packed)) != MOE_OK)
             return rc;
     }
     const void* resid = (flags & MOE_FLAG_NO_RESIDUAL) ? nullptr : u;

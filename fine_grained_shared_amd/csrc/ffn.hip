@@ -19,6 +19,8 @@
 // tiny fp32 layer only).
 #include <stdlib.h>
 
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -420,7 +422,10 @@ __device__ __forceinline__ const bf16x8& frag(const unsigned char* base, int row
 template <int MODE>
 __device__ __forceinline__ void wide_epilogue(const GemmParams& p, const TileInfo& ti, f32x16 (&acc)[4][2],
                                               unsigned char* smem) {
-    const int tid = threadIdx.x;
+    // recomputed here from an opaque copy of the thread index: the epilogue's lane-dependent
+    // addresses are then not kept live (or spilled) across the k-loop and the tile loop
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
     const int lane = tid & 63, w = tid >> 6;
     float* st = reinterpret_cast<float*>(smem);
     if (MODE == GM_UP_SWIGLU) {
@@ -649,6 +654,64 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* ptr, int
                                              0x00020000);
 }
 
+// Epilogue of the four-wave 128 x 512 tile held as acc[i][j] (rows 32 i .., wave w's columns:
+// SwiGLU gate blocks j = 0, 1 and the matching up blocks j = 2, 3 of outputs 64 w .., otherwise
+// 128 w + 32 j): stage the fp32 values through LDS, then 16-byte stores of 8-column row pieces.
+template <int MODE>
+__device__ __forceinline__ void w4_epilogue(const GemmParams& p, const TileInfo& ti, f32x16 (&acc)[4][4],
+                                            unsigned char* smem) {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, w = tid >> 6;
+    float* st = reinterpret_cast<float*>(smem);
+    if (MODE == GM_UP_SWIGLU) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                    const int rl = 32 * i + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+                    st[rl * WEPW_SW + 64 * w + 32 * jj + (lane & 31)] = silu(acc[i][jj][q]) * acc[i][jj + 2][q];
+                }
+        __syncthreads();
+        const int cq = (tid & 31) * 8;
+        const int col0 = ti.nt * 256 + cq;
+        if (col0 < p.N) {
+            for (int rl = tid >> 5; rl < ti.rows; rl += 8) {
+                const float4 v0 = *reinterpret_cast<const float4*>(&st[rl * WEPW_SW + cq]);
+                const float4 v1 = *reinterpret_cast<const float4*>(&st[rl * WEPW_SW + cq + 4]);
+                float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+                epilogue_row<MODE>(p, ti, v, rl, col0);
+            }
+        }
+        return;
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {   // rows [64 h, 64 h + 64)
+        if (h) __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                    const int rl = 32 * i + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+                    st[rl * W4EPW + 128 * w + 32 * j + (lane & 31)] = acc[2 * h + i][j][q];
+                }
+        __syncthreads();
+        const int cq = lane * 8;
+        const int col0 = ti.nt * WBN + cq;
+        if (col0 < p.N) {
+            for (int rl = w; rl < 64 && 64 * h + rl < ti.rows; rl += 4) {
+                const float4 v0 = *reinterpret_cast<const float4*>(&st[rl * W4EPW + cq]);
+                const float4 v1 = *reinterpret_cast<const float4*>(&st[rl * W4EPW + cq + 4]);
+                float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+                epilogue_row<MODE>(p, ti, v, 64 * h + rl, col0);
+            }
+        }
+    }
+}
+
 template <int MODE>
 __device__ __forceinline__ void gemm_tile_w4(const GemmParams& p, const TileInfo& ti, unsigned char* smem) {
     const int tid = threadIdx.x;
@@ -864,6 +927,206 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_w4(GemmParams p, int NT) {
     }
 }
 
+// ---------------------------------------------------------------- packed weights
+// The weights are static, so they can be stored once in the order the MFMA reads its B operand:
+// for every 32-row block nb and 16-wide k-chunk kc of a group's [rows, K] matrix, one contiguous
+// 1 KB fragment at block index nb * (K / 16) + kc, whose 16-byte piece l (l < 64) holds row
+// 32 nb + l % 32, columns 16 kc + 8 (l / 32) .. + 7: exactly the eight bf16 lane l of a wave
+// feeds to v_mfma_f32_32x32x16_bf16.  One 16-byte load per lane then fetches a whole fragment as
+// 1 KB of consecutive bytes, straight into the registers the MFMA reads.
+__global__ __launch_bounds__(256) void k_pack_b(const uint16_t* __restrict__ w, uint16_t* __restrict__ out,
+                                                long long pieces, int N, int K) {
+    const long long per = (long long)N * K / 8;   // 16-byte pieces per matrix
+    const int kcn = K / 16;
+    for (long long i = blockIdx.x * 256LL + threadIdx.x; i < pieces; i += (long long)gridDim.x * 256) {
+        const long long g = i / per;
+        const long long r = i - g * per;
+        const int l = (int)(r & 63);
+        const long long blk = r >> 6;
+        const long long nb = blk / kcn;
+        const int kc = (int)(blk - nb * kcn);
+        const long long n = nb * 32 + (l & 31);
+        const int k = kc * 16 + (l >> 5) * 8;
+        reinterpret_cast<uint4*>(out)[i] = *reinterpret_cast<const uint4*>(w + g * N * (long long)K + n * K + k);
+    }
+}
+
+hipError_t launch_pack_b(const void* w, void* out, int G, int N, int K, hipStream_t s) {
+    const long long pieces = (long long)G * N * K / 8;
+    if (pieces == 0) return hipSuccess;
+    long long nb = (pieces + 255) / 256;
+    nb = nb < 8192 ? nb : 8192;
+    hipLaunchKernelGGL(k_pack_b, dim3((unsigned)nb), dim3(256), 0, s, (const uint16_t*)w, (uint16_t*)out, pieces, N,
+                       K);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- 4-wave 128 x 512 tile, packed weights
+// Same tile and wave split as k_gemm_bf16_w4, but the weight operand is in fragment order: each wave
+// loads its own 16 fragments per k-step (4 row blocks x 4 k-chunks, 16 KB) straight into registers,
+// two k-steps ahead (two register sets), and never touches LDS for them.  Only the A tile, which all
+// four waves read, goes through LDS: direct-to-LDS loads into a ring of four 16 KB stages, filled
+// four k-steps ahead.  Per k-step a workgroup writes 16 KB and reads 64 KB of LDS (the register-staged
+// kernel: 80 KB and 128 KB), and one barrier hands the ring over.
+//
+// Per k-step and wave, in issue order: B loads of k-step kt+2 for chunks 0, 1, 2 (four each, after
+// the last MFMA reading that register), then in chunk 3: vmcnt wait + barrier, the B load of block 0,
+// the four A loads of k-tile kt+4 into the stage k-step kt just finished reading, the B loads of
+// blocks 1-3.  That is 20 vector-memory operations per k-step.
+constexpr int kPStage = BM * BK * 2;   // 16 KB A stage
+constexpr int kPStages = 4;
+// The A loads of k-tile kt+1 (issued in k-step kt-3, or in the prologue) must have landed when k-step
+// kt starts reading them (chunk 3).  At that point at most this many vector-memory operations were
+// issued after them: 52 in k-step 0 (prologue order: A0..A3, B0, B1), 55 in the steady state.
+constexpr int kPWaitA = 52;
+// prologue: A(0) has A1..A3 (12) and B0, B1 (32) issued after it
+constexpr int kPWaitA0 = 44;
+static_assert(kPStages * kPStage <= kWSmem, "A ring must fit");
+
+// A_FLAT: A spans 2 GiB or more, so its loads take 64-bit addresses (global_load_lds).  The compiler
+// counts such a load as a possible LDS access as well, and then waits for every outstanding load
+// (vmcnt(0)) before the next use of a loaded register: correct, but the B prefetch no longer
+// overlaps.  Otherwise A uses buffer loads into LDS with 32-bit offsets, which keep the counts exact.
+template <int MODE, bool A_FLAT>
+__device__ __forceinline__ void gemm_tile_w4p(const GemmParams& p, const TileInfo& ti, unsigned char* smem) {
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));   // per-tile lane values: not hoisted out of the tile loop
+    const int lane = tid & 63, w = tid >> 6;   // w < 4
+    const int nk = p.K / BK;
+    const unsigned kcn = (unsigned)(p.K / 16);
+
+    // B: the group's packed matrix; fragment (nb, kc) of this lane at (nb * kcn + kc) * 1024 + 16 lane
+    const __amdgpu_buffer_rsrc_t rsB = make_rsrc((const uint16_t*)p.B + (size_t)ti.g * p.sB_group, p.b_bytes);
+    unsigned voB[4];
+    {
+        const int nbl = p.N / 32 - 1;   // last row block of the output columns
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            int nb;
+            if (MODE == GM_UP_SWIGLU) {
+                const int t = min(ti.nt * 8 + 2 * w + (j & 1), nbl);
+                nb = j < 2 ? t : p.up_off / 32 + t;
+            } else {
+                nb = min(ti.nt * 16 + 4 * w + j, nbl);
+            }
+            voB[j] = (unsigned)nb * kcn * 1024u + (unsigned)lane * 16u;
+        }
+    }
+    // A: wave w moves 1 KB chunks 4w + i (rows 32 w + 8 i .. + 7) of each k-tile; lane l of a chunk is
+    // row 8c + l / 8, LDS slot l % 8, global chunk (l % 8) ^ ((row >> 1) & 7)
+    const uint16_t* A = (const uint16_t*)p.A;
+    const __amdgpu_buffer_rsrc_t rsA = make_rsrc(p.A, A_FLAT ? 0 : p.a_bytes);
+    const uint16_t* ag[4];
+    unsigned voA[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = 32 * w + 8 * i + (lane >> 3);
+        const int kcg = ((lane & 7) ^ ((row >> 1) & 7)) * 8;
+        const int r = min(row, ti.rows - 1);
+        long long src = ti.row0 + r;
+        if (p.a_rows) src = min(max((long long)p.a_rows[src], 0LL), p.a_nrows - 1);
+        ag[i] = A + src * p.lda + kcg;
+        voA[i] = A_FLAT ? 0u : (unsigned)(src * p.lda + kcg) * 2u;
+    }
+    // A chunk i of k-tile column k (elements) into LDS chunk base dst
+    auto load_a = [&](int i, int k, unsigned char* dst) {
+        if (A_FLAT) dma16(ag[i] + k, dst);
+        else __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, (lds_ptr_t)dst, 16, voA[i], 2 * k, 0, 0);
+    };
+
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+    bf16x8 af[2][4];
+    v4u bq[2][4][4];   // [k-step parity][chunk][row block]
+
+    __syncthreads();   // the previous tile's epilogue may still read the LDS staging area
+#pragma unroll
+    for (int st = 0; st < kPStages; ++st) {
+        const int k = min(st, nk - 1) * BK;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) load_a(i, k, smem + st * kPStage + (4 * w + i) * 1024);
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                bq[t][s][j] = __builtin_amdgcn_raw_buffer_load_b128(rsB, voB[j], min(t, nk - 1) * 4096 + s * 1024, 0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(kPWaitA0, 0));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < 4; ++i) af[0][i] = frag(smem, 32 * i + (lane & 31), lane >> 5);
+
+    auto kstep = [&](const int kt, auto setc) {
+        constexpr int SET = decltype(setc)::value;
+        unsigned char* sa = smem + (kt & 3) * kPStage;               // k-tile kt; refilled with kt+4
+        const unsigned char* sn = smem + ((kt + 1) & 3) * kPStage;   // k-tile kt+1
+        const int kb = min(kt + 2, nk - 1) * 4096;                   // B byte offset of k-tile kt+2
+        const int ka = min(kt + 4, nk - 1) * BK;                     // A column of k-tile kt+4
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            if (s == 3) {
+                // A(kt+1) landed for this wave, then for all (barrier); every wave is done reading
+                // stage kt, which the A loads below refill
+                __builtin_amdgcn_sched_barrier(0);
+                asm volatile("" ::: "memory");
+                __builtin_amdgcn_s_waitcnt(waitcnt_imm(kPWaitA, 0));
+                __builtin_amdgcn_s_barrier();
+                asm volatile("" ::: "memory");
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        af[s & 1][i], __builtin_bit_cast(bf16x8, bq[SET][s][j]), acc[i][j], 0, 0, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (j == 0) {   // A fragments of the next chunk
+                        if (s < 3) af[(s + 1) & 1][i] = frag(sa, 32 * i + (lane & 31), 2 * (s + 1) + (lane >> 5));
+                        else af[0][i] = frag(sn, 32 * i + (lane & 31), lane >> 5);
+                    }
+                    if (s == 3 && j == 1) load_a(i, ka, sa + (4 * w + i) * 1024);
+                    if (i == 3) bq[SET][s][j] = __builtin_amdgcn_raw_buffer_load_b128(rsB, voB[j], kb + s * 1024, 0);
+                }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+        kstep(kt, std::integral_constant<int, 0>());
+        kstep(kt + 1, std::integral_constant<int, 1>());
+    }
+    if (kt < nk) kstep(kt, std::integral_constant<int, 0>());
+    // drain the trailing (clamped) loads before the LDS is reused for staging
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    w4_epilogue<MODE>(p, ti, acc, smem);
+}
+
+template <int MODE, bool A_FLAT>
+__global__ __launch_bounds__(256, 1) void k_gemm_bf16_w4p(GemmParams p, int NT) {
+    __shared__ __attribute__((aligned(16))) unsigned char smem[kWSmem];
+    const int total = total_tiles(p, NT);
+    const int xcd = blockIdx.x & 7, loc = blockIdx.x >> 3, per_xcd = gridDim.x >> 3;
+    const int beg = (int)((long long)total * xcd / 8);
+    const int end = (int)((long long)total * (xcd + 1) / 8);
+    for (int L = beg + loc; L < end; L += per_xcd) {
+        TileInfo ti;
+        decode_tile(p, NT, BM, L, ti);
+        gemm_tile_w4p<MODE, A_FLAT>(p, ti, smem);
+    }
+}
+
 // ---------------------------------------------------------------- decode-shaped grouped GEMM
 // Few rows per group (decode: a handful of tokens per expert) make the expert GEMMs a stream of
 // weight bytes.  Tiles of 32 rows x 256 weight rows x 64 k; four waves, each 32 rows x 64 weight
@@ -879,7 +1142,9 @@ constexpr int kDSmem = DSTAGES * kDStage;        // 144 KB
 constexpr int DEPW = DBN + 4;                    // fp32 staging row of the epilogue
 static_assert(DBM * DEPW * 4 <= kDSmem, "decode epilogue staging must fit");
 
-template <int MODE>
+// PK: the weights are in fragment order (k_pack_b); wave w's eight B chunks are then the fragments of
+// its two 32-row blocks j for the four k-chunks s (chunk 4 j + s), and LDS holds them in that order.
+template <int MODE, bool PK>
 __device__ __forceinline__ void gemm_tile_dec(const GemmParams& p, const TileInfo& ti, unsigned char* smem) {
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;   // w < 4
@@ -900,6 +1165,18 @@ __device__ __forceinline__ void gemm_tile_dec(const GemmParams& p, const TileInf
     const uint16_t* bg[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
+        if (PK) {
+            const int nbl = p.N / 32 - 1, j = i >> 2;
+            int nb;
+            if (MODE == GM_UP_SWIGLU) {
+                const int t = min(ti.nt * (DBN / 64) + w, nbl);
+                nb = j ? p.up_off / 32 + t : t;
+            } else {
+                nb = min(ti.nt * (DBN / 32) + 2 * w + j, nbl);
+            }
+            bg[i] = Bg + (((size_t)nb * (p.K / 16) + (i & 3)) * 64 + lane) * 8;
+            continue;
+        }
         int wr;
         if (MODE == GM_UP_SWIGLU) {
             const int t = 32 * w + 8 * (i & 3) + (lane >> 3);
@@ -914,7 +1191,8 @@ __device__ __forceinline__ void gemm_tile_dec(const GemmParams& p, const TileInf
     auto issue = [&](int kt) {   // k-tile min(kt, nk - 1) into its stage
         const int k = (kt < nk ? kt : nk - 1) * BK;
         const int seg = k / p.Kseg;
-        const long long bo = (long long)seg * p.sB_seg + (k - seg * p.Kseg);
+        // packed: a 64-wide k-tile is four consecutive 1 KB fragments (2048 elements) per row block
+        const long long bo = PK ? (long long)k * 32 : (long long)seg * p.sB_seg + (k - seg * p.Kseg);
         unsigned char* st = smem + (kt % DSTAGES) * kDStage;
         dma16(ag + k, st + w * 1024);
 #pragma unroll
@@ -946,8 +1224,10 @@ __device__ __forceinline__ void gemm_tile_dec(const GemmParams& p, const TileInf
         for (int s = 0; s < BK / 16; ++s) {
             const int kc = 2 * s + (lane >> 5);
             const bf16x8 a = frag(sa, lane & 31, kc);
-            const bf16x8 b0 = frag(sb, 64 * w + (lane & 31), kc);
-            const bf16x8 b1 = frag(sb, 64 * w + 32 + (lane & 31), kc);
+            const bf16x8 b0 = PK ? *reinterpret_cast<const bf16x8*>(sb + (8 * w + s) * 1024 + lane * 16)
+                                 : frag(sb, 64 * w + (lane & 31), kc);
+            const bf16x8 b1 = PK ? *reinterpret_cast<const bf16x8*>(sb + (8 * w + 4 + s) * 1024 + lane * 16)
+                                 : frag(sb, 64 * w + 32 + (lane & 31), kc);
             acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b0, acc0, 0, 0, 0);
             acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b1, acc1, 0, 0, 0);
         }
@@ -986,7 +1266,7 @@ __device__ __forceinline__ void gemm_tile_dec(const GemmParams& p, const TileInf
 
 // Grouped: tiles over the 32-row tile prefix; dense (a few tokens through the shared experts): every
 // group covers rows [0, M_dense) in 32-row tiles.
-template <int MODE, bool GROUPED>
+template <int MODE, bool GROUPED, bool PK = false>
 __global__ __launch_bounds__(256, 1) void k_gemm_bf16_dec(GemmParams p, int NT) {
     if (GROUPED != (p.offsets != nullptr)) return;  // launched with the matching instantiation only
     __shared__ __attribute__((aligned(16))) unsigned char smem[kDSmem];
@@ -1018,7 +1298,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_dec(GemmParams p, int NT) 
             ti.row0 = ml * DBM;
             ti.rows = min(DBM, p.M_dense - ti.row0);
         }
-        gemm_tile_dec<MODE>(p, ti, smem);
+        gemm_tile_dec<MODE, PK>(p, ti, smem);
     }
 }
 
@@ -1097,7 +1377,7 @@ hipError_t launch_gemm(int dtype, int mode, const GemmParams& p_in, hipStream_t 
         p.b_bytes = b_span > 0 && b_span < lim ? (int)b_span : 0;
     }
     if (dtype == 0) {
-        if (mode == GM_DOWN_COMBINE || mode == GM_F32OUT) return hipErrorInvalidValue;  // bf16 modes only
+        if (mode == GM_DOWN_COMBINE || mode == GM_F32OUT || p.packed) return hipErrorInvalidValue;  // bf16 only
         dim3 grid((p.N + 63) / 64, (p.max_rows + 3) / 4, p.offsets ? 1 : p.G);
         if (mode == GM_UP_SWIGLU) hipLaunchKernelGGL(k_gemm_f32<GM_UP_SWIGLU>, grid, dim3(256), 0, s, p);
         else if (mode == GM_UP_RELU) hipLaunchKernelGGL(k_gemm_f32<GM_UP_RELU>, grid, dim3(256), 0, s, p);
@@ -1105,10 +1385,43 @@ hipError_t launch_gemm(int dtype, int mode, const GemmParams& p_in, hipStream_t 
         return hipGetLastError();
     }
     if (mode == GM_DOWN_COMBINE && p.offsets) return hipErrorInvalidValue;  // dense (shared) groups only
+    const long long cus = device_cus();
+    if (p.packed) {
+        // fragment-order weights: routed (grouped) up/down GEMMs, one K segment, 32-bit offsets
+        if (!p.offsets || !p.tiles32 || p.Kseg != p.K || p.b_bytes == 0 || p.N % 32 ||
+            !(mode == GM_UP_SWIGLU || mode == GM_UP_RELU || mode == GM_DOWN))
+            return hipErrorInvalidValue;
+        const long long rpg = p.max_rows / p.G;
+        if (rpg < 64) {   // decode-sized groups: 32-row tiles, deep direct-to-LDS pipeline
+            const int NTd = mode == GM_UP_SWIGLU ? (p.N + DBN / 2 - 1) / (DBN / 2) : (p.N + DBN - 1) / DBN;
+            const long long mtd = (p.max_rows + DBM - 1) / DBM + p.G;
+            long long nb = (mtd * NTd + 7) / 8 * 8;
+            nb = nb < cus ? nb : cus;
+            const dim3 grid((unsigned)((nb + 7) / 8 * 8));
+            if (mode == GM_UP_SWIGLU) hipLaunchKernelGGL((k_gemm_bf16_dec<GM_UP_SWIGLU, true, true>), grid, dim3(256), 0, s, p, NTd);
+            else if (mode == GM_UP_RELU) hipLaunchKernelGGL((k_gemm_bf16_dec<GM_UP_RELU, true, true>), grid, dim3(256), 0, s, p, NTd);
+            else hipLaunchKernelGGL((k_gemm_bf16_dec<GM_DOWN, true, true>), grid, dim3(256), 0, s, p, NTd);
+            return hipGetLastError();
+        }
+        const int NTp = mode == GM_UP_SWIGLU ? (p.N + 255) / 256 : (p.N + WBN - 1) / WBN;
+        const long long mtp = (p.max_rows + BM - 1) / BM + p.G;
+        long long nb = (mtp * NTp + 7) / 8 * 8;
+        nb = nb < cus ? nb : cus;
+        const dim3 grid((unsigned)((nb + 7) / 8 * 8));
+#define MOE_LAUNCH_P(M)                                                                                       \
+    do {                                                                                                      \
+        if (p.a_bytes > 0) hipLaunchKernelGGL((k_gemm_bf16_w4p<M, false>), grid, dim3(256), 0, s, p, NTp);   \
+        else hipLaunchKernelGGL((k_gemm_bf16_w4p<M, true>), grid, dim3(256), 0, s, p, NTp);                   \
+    } while (0)
+        if (mode == GM_UP_SWIGLU) MOE_LAUNCH_P(GM_UP_SWIGLU);
+        else if (mode == GM_UP_RELU) MOE_LAUNCH_P(GM_UP_RELU);
+        else MOE_LAUNCH_P(GM_DOWN);
+#undef MOE_LAUNCH_P
+        return hipGetLastError();
+    }
     long long mt;  // upper bound of the m-tile count (grouped: sum of ceil(rows_g / BM) <= R / BM + G)
     if (p.offsets) mt = (p.max_rows + BM - 1) / BM + p.G;
     else mt = (long long)p.G * ((p.M_dense + BM - 1) / BM);
-    const long long cus = device_cus();
     const int NTw = mode == GM_UP_SWIGLU ? (p.N + 255) / 256 : (p.N + WBN - 1) / WBN;
     // the 128 x 512 tile pays off only with many rows per group (prefill); decode-sized groups
     // (a few rows per expert) stream their weights better through the 128 x 128 tile

@@ -72,6 +72,8 @@ struct GemmParams {
     // (kernels addressing them with 32-bit buffer offsets are chosen only then), else 0
     int a_bytes;
     int b_bytes;
+    // weights in MFMA fragment order (launch_pack_b); grouped bf16 up/down GEMMs with one K segment only
+    int packed;
 };
 // m-tile prefixes of the groups defined by offsets (grouped mode): tiles[0..G] for tiles of bm rows,
 // tiles[G+1 .. 2G+1] for tiles of 32 rows.
@@ -79,6 +81,9 @@ constexpr int kTilePlans = 2;
 hipError_t launch_tile_plan(const int32_t* offsets, int G, int bm, int32_t* tiles, hipStream_t s);
 int gemm_bm(int dtype);
 hipError_t launch_gemm(int dtype, int mode, const GemmParams& p, hipStream_t s);
+// G bf16 matrices [N, K] -> fragment order: 1 KB block nb * (K / 16) + kc holds rows 32 nb .. + 31,
+// columns 16 kc .. + 15, 16-byte piece l = row 32 nb + l % 32, columns 16 kc + 8 (l / 32) .. + 7
+hipError_t launch_pack_b(const void* w, void* out, int G, int N, int K, hipStream_t s);
 
 // ---------------------------------------------------------------- combine, controller
 hipError_t launch_combine(int dtype, const void* residual, const void* y_shared, const void* y_perm,

@@ -73,7 +73,10 @@ enum { MOE_ACT_RELU_BIAS = 0, MOE_ACT_SWIGLU = 1 };
 enum { MOE_F32 = 0, MOE_BF16 = 1 };
 
 /* moe_layer_forward flags */
-enum { MOE_FLAG_NO_RESIDUAL = 1 }; /* drop the + u_t term: returns the MoE part only */
+enum {
+    MOE_FLAG_NO_RESIDUAL = 1,   /* drop the + u_t term: returns the MoE part only */
+    MOE_FLAG_PACKED_WEIGHTS = 2 /* routed banks w1, w2 are in fragment order (moe_pack_weights) */
+};
 
 typedef struct moe_shape {
     int32_t T;          /* tokens */
@@ -143,6 +146,28 @@ int moe_expert_ffn(const moe_shape* shape, const void* x, const int32_t* row_tok
                    void* stream);
 
 /*
+ * Weight repacking for the routed experts (a storage layout of the same FFN weights; the result of
+ * every FFN is bit-identical to the one computed from the [out, in] banks).  Expert weights are
+ * static, so they can be stored once in the order in which the matrix cores read them: G bf16
+ * matrices [N, K] (row-major) become, per matrix, (N / 32) * (K / 16) blocks of 1 KB; block
+ * nb * (K / 16) + kc holds rows 32 nb .. 32 nb + 31 and columns 16 kc .. 16 kc + 15, and its
+ * 16-byte piece l (0 <= l < 64) holds row 32 nb + l % 32, columns 16 kc + 8 (l / 32) .. + 7.
+ * `packed` has the size of `w` (G*N*K*2 bytes) and must not overlap it; both 16-byte aligned.
+ * N % 32 == 0 and K % 64 == 0 (else MOE_ERR_INVALID_ARG); N*K*2 < 2^31 (else MOE_ERR_UNSUPPORTED).
+ * Routed banks: w1 with (G, N, K) = (N_r, 2I, H) (SwiGLU) or (N_r, I, H) (ReLU), w2 with (N_r, H, I).
+ * Enqueued on `stream` like every call; pack once when the weights are loaded.
+ */
+int moe_pack_weights(const void* w, void* packed, int32_t G, int32_t N, int32_t K, void* stream);
+
+/*
+ * moe_expert_ffn with w1 and w2 in the packed order of moe_pack_weights (bf16 only; fp32 ->
+ * MOE_ERR_INVALID_ARG).  Same arguments, same results bit for bit.
+ */
+int moe_expert_ffn_packed(const moe_shape* shape, const void* x, const int32_t* row_token,
+                          const int32_t* offsets, const void* w1, const float* b1, const void* w2, void* y,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Shared experts (DeepSeekMoE Eq. 9, first term): y[t] = sum_{j<Ks} FFN^shared_j(x[t]) for all
  * T tokens, computed as one FFN of width Ks*I (the Ks experts' intermediate rows side by side).
  *   x [T, H]; w1_sh, b1_sh, w2_sh banks with G = Ks; y [T, H] dtype out.  Ks == 0 -> MOE_OK, no work.
@@ -162,6 +187,8 @@ int moe_combine(const moe_shape* shape, const void* residual, const void* y_shar
  * The whole layer: route -> dispatch -> routed FFNs + shared FFNs -> combine + residual.
  *   u [T, H]; centroids [N_r, H]; bias [N_r] | NULL; routed banks (G = N_r); shared banks
  *   (G = Ks, NULL when Ks == 0); flags: MOE_FLAG_*; out [T, H] dtype.
+ *   MOE_FLAG_PACKED_WEIGHTS: w1 and w2 (routed) are packed by moe_pack_weights (bf16 only); the
+ *   shared banks stay [out, in]; the output is bit-identical to the unpacked call.
  *   topk_idx_out [T, K_r], topk_w_out [T, K_r]: optional copies of the routing (NULL = none).
  */
 int moe_layer_forward(const moe_shape* shape, const void* u, const void* centroids, const float* bias,

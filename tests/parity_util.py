@@ -70,6 +70,7 @@ class Case:
         s = shape if shape is not None else gpu_shape(self.w)
         d = self.dev
         b = d["bias"] if bias == "default" else bias
+        flags |= getattr(self, "extra_flags", 0)   # e.g. MOE_FLAG_PACKED_WEIGHTS for packed routed banks
         return moe.layer_forward(s, d["u"] if u is None else u, d["centroids"], b, d["w1"], d["b1"], d["w2"],
                                  d["w1_sh"], d["b1_sh"], d["w2_sh"], flags=flags)
 

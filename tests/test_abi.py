@@ -77,6 +77,34 @@ def test_calls_rejected_before_any_launch():
         moe.MOE_ERR_INVALID_ARG
 
 
+def test_packed_weight_calls_rejected_before_any_launch():
+    """moe_pack_weights / moe_expert_ffn_packed / MOE_FLAG_PACKED_WEIGHTS argument checks (host only:
+    the pointers are never dereferenced because every case is rejected before a launch)."""
+    import ctypes
+    lib = moe.load()
+    A, B = 1 << 20, 1 << 30   # 16-byte aligned stand-ins, far apart
+    assert lib.moe_pack_weights(A, B, 2, 48, 128, None) == moe.MOE_ERR_INVALID_ARG    # N % 32
+    assert lib.moe_pack_weights(A, B, 2, 64, 96, None) == moe.MOE_ERR_INVALID_ARG     # K % 64
+    assert lib.moe_pack_weights(A, B, -1, 64, 64, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_pack_weights(A, A + 4096, 1, 64, 64, None) == moe.MOE_ERR_INVALID_ARG  # overlap
+    assert lib.moe_pack_weights(A + 8, B, 1, 64, 64, None) == moe.MOE_ERR_INVALID_ARG     # alignment
+    assert lib.moe_pack_weights(None, B, 1, 64, 64, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_pack_weights(A, B, 1, 32768, 65536, None) == moe.MOE_ERR_UNSUPPORTED   # 4 GiB matrix
+    assert lib.moe_pack_weights(None, None, 0, 64, 64, None) == moe.MOE_OK               # nothing to pack
+    # fp32 layers have no packed form
+    s32 = moe.make_shape(16, 128, 16, 4, 1, 64, 0, 1, moe.MOE_F32)
+    assert lib.moe_expert_ffn_packed(ctypes.byref(s32), A, None, A, A, None, A, A, A, 1 << 30, None) == \
+        moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_layer_forward(ctypes.byref(s32), None, None, None, None, None, None, None, None, None,
+                                 moe.MOE_FLAG_PACKED_WEIGHTS, None, None, None, None, 0, None) == \
+        moe.MOE_ERR_INVALID_ARG
+    # bf16 with too large an expert matrix for 32-bit offsets
+    sbig = moe.make_shape(16, 65536, 16, 4, 0, 16384, 0, 1, moe.MOE_BF16)
+    assert lib.moe_layer_forward(ctypes.byref(sbig), None, None, None, None, None, None, None, None, None,
+                                 moe.MOE_FLAG_PACKED_WEIGHTS, None, None, None, None, 0, None) == \
+        moe.MOE_ERR_UNSUPPORTED
+
+
 def test_no_kernel_uses_scratch_memory():
     """Every HIP kernel keeps its working set in registers/LDS (hipcc resource report): at most a
     few spilled registers, no arrays in scratch memory."""

@@ -5,7 +5,9 @@ The projections that read the activations (routed and shared up) cannot use 32-b
 offsets there and run on the 128 x 512 kernel with 64-bit addressing and direct-to-LDS loads;
 the down projections (the shared one with the fused combine) read the 156 MB / 78 MB hidden
 activations and stay on the buffer-load kernel.  The layer output is checked on a sample of
-tokens against the oracle, routing on the same sample.
+tokens against the oracle, routing on the same sample.  With the routed banks packed
+(fragment order), the routed up projection takes the packed kernel's 64-bit-address variant;
+its output must be bit-identical to the unpacked layer's.
 """
 import gc
 
@@ -28,7 +30,20 @@ def test_activations_beyond_2gib():
     say("[large] generating %.2f GB of activations" % (w.T * w.H * 2 / 1e9))
     case = Case(w)
     try:
-        layer_parity(case, tokens=sample_tokens(w.T, 48), route_all=False, label="big_u")
+        _, (out, idx, _) = layer_parity(case, tokens=sample_tokens(w.T, 48), route_all=False, label="big_u")
+        import fine_grained_shared_amd as moe
+        pcase = Case.__new__(Case)
+        pcase.w, pcase.inp = case.w, case.inp
+        pcase.dev = dict(case.dev)
+        pcase.dev["w1"] = moe.pack_weights(case.dev["w1"])
+        pcase.dev["w2"] = moe.pack_weights(case.dev["w2"])
+        pcase.extra_flags = moe.MOE_FLAG_PACKED_WEIGHTS
+        pout, pidx, _ = pcase.forward()
+        torch.cuda.synchronize()
+        assert torch.equal(idx, pidx)
+        assert torch.equal(out.view(torch.int16), pout.view(torch.int16)), "packed layer differs"
+        say("[large] packed routed banks: bit-identical")
+        pcase.dev.clear()
     finally:
         case.dev.clear()
         case.inp.clear()
