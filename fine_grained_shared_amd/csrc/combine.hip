@@ -33,10 +33,10 @@ __device__ __forceinline__ void store8(E* p, const float (&v)[8]);
 template <>
 __device__ __forceinline__ void store8<uint16_t>(uint16_t* p, const float (&v)[8]) {
     uint4 q;
-    q.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-    q.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
-    q.z = (uint32_t)f32_to_bf16(v[4]) | ((uint32_t)f32_to_bf16(v[5]) << 16);
-    q.w = (uint32_t)f32_to_bf16(v[6]) | ((uint32_t)f32_to_bf16(v[7]) << 16);
+    q.x = pack2_bf16(v[0], v[1]);
+    q.y = pack2_bf16(v[2], v[3]);
+    q.z = pack2_bf16(v[4], v[5]);
+    q.w = pack2_bf16(v[6], v[7]);
     *reinterpret_cast<uint4*>(p) = q;
 }
 template <>

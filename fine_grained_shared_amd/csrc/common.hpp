@@ -14,11 +14,16 @@ constexpr int kWave = 64;
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
-// Round to nearest even; inputs are finite by contract.
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-    uint32_t x = __float_as_uint(f);
-    x += 0x7FFFu + ((x >> 16) & 1u);
-    return (uint16_t)(x >> 16);
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32); inputs are finite by contract.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+
+// Two values in one conversion: lo in bits 15:0, hi in bits 31:16.
+__device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
+    const f32x2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 // Element access for the two storage types (float, or bf16 bits in uint16_t).
@@ -48,7 +53,9 @@ __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v)
     return v;
 }
 
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+// SiLU of the bf16 path with the hardware reciprocal (about 1 ulp of fp32) in place of an IEEE
+// division: the result is rounded to bf16 (8 significant bits) right after.
+__device__ __forceinline__ float silu(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 // Map a workgroup id to a logical tile id so that the workgroups that run on one XCD
 // (ids b with equal b % 8, dispatched round-robin) take consecutive logical tiles and

@@ -196,10 +196,10 @@ __device__ __forceinline__ void mma_tile(f32x16& c00, f32x16& c01, f32x16& c10, 
 
 __device__ __forceinline__ uint4 pack8_bf16(const float (&v)[8]) {
     uint4 o;
-    o.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-    o.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
-    o.z = (uint32_t)f32_to_bf16(v[4]) | ((uint32_t)f32_to_bf16(v[5]) << 16);
-    o.w = (uint32_t)f32_to_bf16(v[6]) | ((uint32_t)f32_to_bf16(v[7]) << 16);
+    o.x = pack2_bf16(v[0], v[1]);
+    o.y = pack2_bf16(v[2], v[3]);
+    o.z = pack2_bf16(v[4], v[5]);
+    o.w = pack2_bf16(v[6], v[7]);
     return o;
 }
 

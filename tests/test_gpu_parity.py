@@ -359,3 +359,35 @@ def test_graph_capture_replays_match_eager(ragged, torch_cuda):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, ref), "replay %d differs from eager" % i
+
+
+def test_bf16_output_rounding_is_nearest_even(torch_cuda):
+    """Outputs are rounded fp32 -> bf16 to nearest, ties to even: residual + shared sums that fall
+    exactly halfway between two bf16 values (exact in fp32) must go to the even neighbour."""
+    import fine_grained_shared_amd as moe
+    torch = torch_cuda
+    e7, e8, e15, e16 = 2.0 ** -7, 2.0 ** -8, 2.0 ** -15, 2.0 ** -16
+    cases = [  # (residual, shared, expected bf16 value)
+        (1 + e7, e8, 1 + 2 * e7),          # 1 + 3*2^-8: tie between odd 1+2^-7 and even 1+2^-6 -> up
+        (1.0, e8, 1.0),                    # 1 + 2^-8: tie between even 1.0 and odd 1+2^-7 -> down
+        (-(1 + e7), -e8, -(1 + 2 * e7)),   # negative tie -> away from the odd neighbour
+        (1.0, e8 + e15, 1 + e7),           # just above the tie -> up
+        (1 + e7, e8 - e16, 1 + e7),        # just below the tie -> down
+        (3.0, 0.0, 3.0),
+        (0.0, 0.0, 0.0),
+    ]
+    H = 64
+    r = np.zeros((1, H), dtype=np.float32)
+    s = np.zeros((1, H), dtype=np.float32)
+    want = np.zeros((1, H), dtype=np.float32)
+    for i, (a, b, c) in enumerate(cases):
+        r[0, i], s[0, i], want[0, i] = a, b, c
+    rt = torch.from_numpy(r).cuda().bfloat16()
+    st = torch.from_numpy(s).cuda().bfloat16()
+    assert torch.equal(rt.float().cpu(), torch.from_numpy(r)) and torch.equal(st.float().cpu(), torch.from_numpy(s))
+    out = torch.empty((1, H), dtype=torch.bfloat16, device="cuda")
+    shape = moe.make_shape(1, H, 1, 0, 1, 64, 0, 1, moe.MOE_BF16)
+    moe.moe_combine(shape, rt, st, None, None, None, out)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    assert np.array_equal(got, want), (got[0, :len(cases)], want[0, :len(cases)])

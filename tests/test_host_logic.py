@@ -67,12 +67,15 @@ def test_gpus_above_one_exit_with_a_message(capsys):
 
 
 def test_traffic_is_reported_only_for_the_measured_source(tmp_path, monkeypatch):
-    t = {"traffic_bytes_per_launch": 123.0, "source_sha256": bench.kernel_source_hash()}
+    k = bench.dominant_kernel(0)
+    t = {"traffic_bytes_per_launch": 123.0, "source_sha256": bench.kernel_source_hash(), "dominant_kernel": k}
     p = tmp_path / "t.json"
     p.write_text(json.dumps(t))
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(p))
     monkeypatch.setattr(bench, "ROOT", bench.ROOT)
-    assert bench.measured_traffic() == 123.0
+    assert bench.measured_traffic(k) == 123.0
+    # counters of the other dominant kernel (the other weight layout) are not reported
+    assert bench.measured_traffic(bench.dominant_kernel(1)) is None
     t["source_sha256"] = "0" * 64
     p.write_text(json.dumps(t))
-    assert bench.measured_traffic() is None
+    assert bench.measured_traffic(k) is None
