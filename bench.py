@@ -4,7 +4,10 @@ One step = one call of moe_layer_forward (router, dispatch, routed + shared expe
 combine + residual) over the V3-style workload: T=16384 tokens, H=7168, 1 shared + 256 routed
 SwiGLU experts of width 2048, top-8, sigmoid + selection bias, bf16 with fp32 accumulation.
 Inputs are seeded synthetic tensors of that shape (no trained weights), resident in HBM before
-timing starts.  The decode regime (the first 128 tokens of the same inputs) is timed as well.
+timing starts.  The routed expert weights are stored in fragment order by default (moe_pack_weights,
+done once when the weights are loaded, outside the timed steps; --weights unpacked keeps the
+[out, in] layout, with bit-identical results).  The decode regime (the first 128 tokens of the
+same inputs) is timed as well.
 
 Prints one JSON line.  Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -297,9 +300,10 @@ def main():
     ap.add_argument("--pmc-fetch", metavar="DIR")
     ap.add_argument("--pmc-write", metavar="DIR")
     ap.add_argument("--traffic-json", metavar="FILE")
-    ap.add_argument("--weights", choices=("packed", "unpacked"), default="unpacked",
-                    help="routed expert banks in fragment order (moe_pack_weights, done once before timing) "
-                         "or in the [out, in] layout")
+    ap.add_argument("--weights", choices=("packed", "unpacked"), default="packed",
+                    help="routed expert banks in fragment order (moe_pack_weights, done once when the weights "
+                         "are loaded, before timing; the layer's output is bit-identical) or in the [out, in] "
+                         "layout")
     args = ap.parse_args()
     if args.rocprof_summary:
         text, _ = rocprof_summary(args.rocprof_summary, args.pmc_fetch, args.pmc_write, args.traffic_json)
