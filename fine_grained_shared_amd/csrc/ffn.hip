@@ -983,6 +983,79 @@ constexpr int kPWaitA = 52;
 constexpr int kPWaitA0 = 44;
 static_assert(kPStages * kPStage <= kWSmem, "A ring must fit");
 
+// Epilogue of the packed kernel (grouped bf16 modes: SwiGLU, ReLU, down).  Each lane holds, for every
+// 32 x 32 accumulator block, rows 8 (q / 4) + 4 (lane / 32) + q % 4 of column lane % 32; the values are
+// finished in registers (SwiGLU, bias + ReLU) and rounded to bf16 two rows at a time (rows r and r+1 of
+// one column in one 32-bit word), so the whole tile is staged in one pass at half the bytes of fp32:
+// word [row pair][column].  Threads then read the words of 8 columns of a row pair, separate the two
+// rows with byte permutes and store 16 bytes per row.  Row pairs are padded by 16 words, so the two
+// half-waves of a staging write fall in disjoint LDS banks.
+template <int MODE>
+__device__ __forceinline__ void w4p_epilogue(const GemmParams& p, const TileInfo& ti, f32x16 (&acc)[4][4],
+                                             unsigned char* smem) {
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));   // lane values recomputed here, not kept live across the k-loop
+    const int lane = tid & 63, w = tid >> 6;
+    constexpr int OUTW = MODE == GM_UP_SWIGLU ? 256 : WBN;   // output columns of the tile
+    constexpr int SW = OUTW + 16;                            // staged words per row pair
+    constexpr int NJ = MODE == GM_UP_SWIGLU ? 2 : 4;         // output column blocks per wave
+    static_assert(BM / 2 * SW * 4 <= kWSmem, "bf16 staging must fit");
+    uint32_t* st = reinterpret_cast<uint32_t*>(smem);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int jb = 0; jb < NJ; ++jb) {
+            const int cl = (MODE == GM_UP_SWIGLU ? 64 * w : 128 * w) + 32 * jb + (lane & 31);   // tile column
+            float bias = 0.f;
+            if (MODE == GM_UP_RELU && p.bias) {
+                const int col = min(ti.nt * OUTW + cl, p.N - 1);
+                bias = p.bias[(long long)ti.g * p.sbias_group + col];
+            }
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+#pragma unroll
+                for (int b = 0; b < 4; b += 2) {
+                    const int q = 4 * a + b;
+                    float x0, x1;
+                    if (MODE == GM_UP_SWIGLU) {
+                        x0 = silu(acc[i][jb][q]) * acc[i][jb + 2][q];
+                        x1 = silu(acc[i][jb][q + 1]) * acc[i][jb + 2][q + 1];
+                    } else if (MODE == GM_UP_RELU) {
+                        x0 = fmaxf(acc[i][jb][q] + bias, 0.0f);
+                        x1 = fmaxf(acc[i][jb][q + 1] + bias, 0.0f);
+                    } else {
+                        x0 = acc[i][jb][q];
+                        x1 = acc[i][jb][q + 1];
+                    }
+                    const int rp = 16 * i + 4 * a + 2 * (lane >> 5) + (b >> 1);   // (32 i + r) / 2
+                    st[rp * SW + cl] = pack2_bf16(x0, x1);
+                }
+        }
+    __syncthreads();
+    constexpr int G = OUTW / 8;   // 8-column groups per row pair
+    uint16_t* C = (uint16_t*)p.C;
+    for (int it = tid; it < BM / 2 * G; it += 256) {
+        const int rp = it / G, cg = it - rp * G;
+        const int r0 = 2 * rp;
+        const int col0 = ti.nt * OUTW + 8 * cg;
+        if (r0 >= ti.rows || col0 >= p.N) continue;
+        const uint4 x = *reinterpret_cast<const uint4*>(&st[rp * SW + 8 * cg]);
+        const uint4 y = *reinterpret_cast<const uint4*>(&st[rp * SW + 8 * cg + 4]);
+        uint4 lo, hi;   // row r0: low halves of the words, row r0 + 1: high halves
+        lo.x = __builtin_amdgcn_perm(x.y, x.x, 0x05040100u);
+        lo.y = __builtin_amdgcn_perm(x.w, x.z, 0x05040100u);
+        lo.z = __builtin_amdgcn_perm(y.y, y.x, 0x05040100u);
+        lo.w = __builtin_amdgcn_perm(y.w, y.z, 0x05040100u);
+        hi.x = __builtin_amdgcn_perm(x.y, x.x, 0x07060302u);
+        hi.y = __builtin_amdgcn_perm(x.w, x.z, 0x07060302u);
+        hi.z = __builtin_amdgcn_perm(y.y, y.x, 0x07060302u);
+        hi.w = __builtin_amdgcn_perm(y.w, y.z, 0x07060302u);
+        const long long row = ti.row0 + r0;
+        *reinterpret_cast<uint4*>(C + row * p.ldc + col0) = lo;
+        if (r0 + 1 < ti.rows) *reinterpret_cast<uint4*>(C + (row + 1) * p.ldc + col0) = hi;
+    }
+}
+
 // A_FLAT: A spans 2 GiB or more, so its loads take 64-bit addresses (global_load_lds).  The compiler
 // counts such a load as a possible LDS access as well, and then waits for every outstanding load
 // (vmcnt(0)) before the next use of a loaded register: correct, but the B prefetch no longer
@@ -1110,7 +1183,7 @@ __device__ __forceinline__ void gemm_tile_w4p(const GemmParams& p, const TileInf
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    w4_epilogue<MODE>(p, ti, acc, smem);
+    w4p_epilogue<MODE>(p, ti, acc, smem);
 }
 
 template <int MODE, bool A_FLAT>
