@@ -628,6 +628,14 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
+// Tile order of the one-workgroup-per-CU GEMMs: all workgroups walk one window of gridDim.x
+// consecutive tiles of the list at a time, and in it XCD x takes the x-th run of per_xcd consecutive
+// tiles.  Inside an XCD the concurrently running tiles share operands through its L2 (blocked m/n
+// order); across XCDs the window covers the same few experts at the same time, so what one XCD reads
+// from HBM the others find in the shared last-level (infinity) cache, instead of eight XCDs streaming
+// eight different experts' weights (more than that cache holds) and re-reading them from HBM.
+__device__ __forceinline__ int window_tile(int xcd, int loc, int per_xcd) { return per_xcd * xcd + loc; }
+
 // ---------------------------------------------------------------- 4-wave 128 x 512 tile
 // Four waves (one per SIMD), each owning a 128 x 128 block of the 128 x 512 tile (4 x 4
 // accumulators of 32 x 32 in the accumulator registers).  Per k-step each wave reads all 128 A
@@ -918,9 +926,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_w4(GemmParams p, int NT) {
     __shared__ __attribute__((aligned(16))) unsigned char smem[kWSmem];
     const int total = total_tiles(p, NT);
     const int xcd = blockIdx.x & 7, loc = blockIdx.x >> 3, per_xcd = gridDim.x >> 3;
-    const int beg = (int)((long long)total * xcd / 8);
-    const int end = (int)((long long)total * (xcd + 1) / 8);
-    for (int L = beg + loc; L < end; L += per_xcd) {
+    for (int L = window_tile(xcd, loc, per_xcd); L < total; L += (int)gridDim.x) {
         TileInfo ti;
         decode_tile(p, NT, BM, L, ti);
         gemm_tile_w4<MODE>(p, ti, smem);
@@ -1191,9 +1197,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_w4p(GemmParams p, int NT) 
     __shared__ __attribute__((aligned(16))) unsigned char smem[kWSmem];
     const int total = total_tiles(p, NT);
     const int xcd = blockIdx.x & 7, loc = blockIdx.x >> 3, per_xcd = gridDim.x >> 3;
-    const int beg = (int)((long long)total * xcd / 8);
-    const int end = (int)((long long)total * (xcd + 1) / 8);
-    for (int L = beg + loc; L < end; L += per_xcd) {
+    for (int L = window_tile(xcd, loc, per_xcd); L < total; L += (int)gridDim.x) {
         TileInfo ti;
         decode_tile(p, NT, BM, L, ti);
         gemm_tile_w4p<MODE, A_FLAT>(p, ti, smem);
