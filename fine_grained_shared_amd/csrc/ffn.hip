@@ -652,6 +652,10 @@ constexpr int W4EPW = WBN + 4;   // non-SwiGLU staging row (512 outputs, 64 rows
 
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
+// Buffer offset of a padding row: past every buffer these kernels address (spans stay below 2^31), so
+// the load returns zeros.
+constexpr unsigned kZeroRow = 0x80000000u;
+
 // Buffer resource over [ptr, ptr + bytes) for 16-byte loads with a per-lane 32-bit byte offset and a
 // wave-uniform scalar byte offset.  The base is made wave-uniform explicitly.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* ptr, int bytes) {
@@ -742,7 +746,7 @@ __device__ __forceinline__ void gemm_tile_w4(const GemmParams& p, const TileInfo
         const int r = min(row, ti.rows - 1);
         long long src = ti.row0 + r;
         if (p.a_rows) src = min(max((long long)p.a_rows[src], 0LL), p.a_nrows - 1);
-        voA[i] = (unsigned)(src * p.lda + ((i & 1) ? kcg1 : kcg0)) * 2u;
+        voA[i] = row < ti.rows ? (unsigned)(src * p.lda + ((i & 1) ? kcg1 : kcg0)) * 2u : kZeroRow;   // padding: zeros
     }
     unsigned voB[16];   // byte offset of B chunk 16w + i of this lane within the group's weights
     {
@@ -1105,7 +1109,9 @@ __device__ __forceinline__ void gemm_tile_w4p(const GemmParams& p, const TileInf
         long long src = ti.row0 + r;
         if (p.a_rows) src = min(max((long long)p.a_rows[src], 0LL), p.a_nrows - 1);
         ag[i] = A + src * p.lda + kcg;
-        voA[i] = A_FLAT ? 0u : (unsigned)(src * p.lda + kcg) * 2u;
+        // padding rows of a group's last m-tile load zeros (an offset past the buffer reads 0): their
+        // products are never stored, and zero operands cost the matrix cores less power
+        voA[i] = A_FLAT ? 0u : (row < ti.rows ? (unsigned)(src * p.lda + kcg) * 2u : kZeroRow);
     }
     // A chunk i of k-tile column k (elements) into LDS chunk base dst
     auto load_a = [&](int i, int k, unsigned char* dst) {
