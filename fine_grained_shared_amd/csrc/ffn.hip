@@ -1114,9 +1114,11 @@ __device__ __forceinline__ void gemm_tile_w4p(const GemmParams& p, const TileInf
         voA[i] = A_FLAT ? 0u : (row < ti.rows ? (unsigned)(src * p.lda + kcg) * 2u : kZeroRow);
     }
     // A chunk i of k-tile column k (elements) into LDS chunk base dst
-    auto load_a = [&](int i, int k, unsigned char* dst) {
+    // zero: OR-ed into the offset (kZeroRow or 0) of the k-tiles past the end that keep the issue
+    // pattern uniform: they read zeros instead of fetching a k-tile again
+    auto load_a = [&](int i, int k, unsigned char* dst, unsigned zero) {
         if (A_FLAT) dma16(ag[i] + k, dst);
-        else __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, (lds_ptr_t)dst, 16, voA[i], 2 * k, 0, 0);
+        else __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, (lds_ptr_t)dst, 16, voA[i] | zero, 2 * k, 0, 0);
     };
 
     f32x16 acc[4][4];
@@ -1134,7 +1136,7 @@ __device__ __forceinline__ void gemm_tile_w4p(const GemmParams& p, const TileInf
     for (int st = 0; st < kPStages; ++st) {
         const int k = min(st, nk - 1) * BK;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) load_a(i, k, smem + st * kPStage + (4 * w + i) * 1024);
+        for (int i = 0; i < 4; ++i) load_a(i, k, smem + st * kPStage + (4 * w + i) * 1024, st < nk ? 0u : kZeroRow);
     }
 #pragma unroll
     for (int t = 0; t < 2; ++t)
@@ -1142,7 +1144,8 @@ __device__ __forceinline__ void gemm_tile_w4p(const GemmParams& p, const TileInf
         for (int s = 0; s < 4; ++s)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                bq[t][s][j] = __builtin_amdgcn_raw_buffer_load_b128(rsB, voB[j], min(t, nk - 1) * 4096 + s * 1024, 0);
+                bq[t][s][j] = __builtin_amdgcn_raw_buffer_load_b128(rsB, voB[j] | (t < nk ? 0u : kZeroRow),
+                                                                    min(t, nk - 1) * 4096 + s * 1024, 0);
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(kPWaitA0, 0));
     __builtin_amdgcn_s_barrier();
@@ -1156,6 +1159,7 @@ __device__ __forceinline__ void gemm_tile_w4p(const GemmParams& p, const TileInf
         const unsigned char* sn = smem + ((kt + 1) & 3) * kPStage;   // k-tile kt+1
         const int kb = min(kt + 2, nk - 1) * 4096;                   // B byte offset of k-tile kt+2
         const int ka = min(kt + 4, nk - 1) * BK;                     // A column of k-tile kt+4
+        const unsigned zb = kt + 2 < nk ? 0u : kZeroRow, za = kt + 4 < nk ? 0u : kZeroRow;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             if (s == 3) {
@@ -1179,8 +1183,9 @@ __device__ __forceinline__ void gemm_tile_w4p(const GemmParams& p, const TileInf
                         if (s < 3) af[(s + 1) & 1][i] = frag(sa, 32 * i + (lane & 31), 2 * (s + 1) + (lane >> 5));
                         else af[0][i] = frag(sn, 32 * i + (lane & 31), lane >> 5);
                     }
-                    if (s == 3 && j == 1) load_a(i, ka, sa + (4 * w + i) * 1024);
-                    if (i == 3) bq[SET][s][j] = __builtin_amdgcn_raw_buffer_load_b128(rsB, voB[j], kb + s * 1024, 0);
+                    if (s == 3 && j == 1) load_a(i, ka, sa + (4 * w + i) * 1024, za);
+                    if (i == 3)
+                        bq[SET][s][j] = __builtin_amdgcn_raw_buffer_load_b128(rsB, voB[j] | zb, kb + s * 1024, 0);
                 }
         }
         __builtin_amdgcn_sched_barrier(0);
