@@ -1232,22 +1232,31 @@ static_assert(DBM * DEPW * 4 <= kDSmem, "decode epilogue staging must fit");
 
 // PK: the weights are in fragment order (k_pack_b); wave w's eight B chunks are then the fragments of
 // its two 32-row blocks j for the four k-chunks s (chunk 4 j + s), and LDS holds them in that order.
-template <int MODE, bool PK>
+// W: waves per workgroup; the tile is 32 rows x 64 W weight rows, each wave owning 64 weight rows.
+// W = 1 serves dense GEMMs of a few rows (the shared experts of a decode step), whose few 256-wide
+// tiles would leave most CUs idle.
+template <int MODE, bool PK, int W = 4>
 __device__ __forceinline__ void gemm_tile_dec(const GemmParams& p, const TileInfo& ti, unsigned char* smem) {
+    constexpr int TN = 64 * W;                         // weight rows of the tile
+    constexpr int NA = 4 / W;                          // activation chunks (8 rows each) per wave
+    constexpr int STAGE = kDTileA + TN * BK * 2;
+    constexpr int STG = DSTAGES;                       // ring stages; STG - 1 k-tiles in flight
     const int tid = threadIdx.x;
-    const int lane = tid & 63, w = tid >> 6;   // w < 4
+    const int lane = tid & 63, w = tid >> 6;   // w < W
     const uint16_t* A = (const uint16_t*)p.A;
     const uint16_t* Bg = (const uint16_t*)p.B + (size_t)ti.g * p.sB_group;
     // chunk permutation of a lane (chunk c of LDS row r holds global chunk c ^ ((r >> 1) & 7))
     const int kcg0 = ((lane & 7) ^ ((lane >> 4) & 7)) * 8;
     const int kcg1 = ((lane & 7) ^ ((4 + (lane >> 4)) & 7)) * 8;
-    // A chunk w: tile rows 8 w .. 8 w + 7
-    const uint16_t* ag;
-    {
-        const int r = min(8 * w + (lane >> 3), ti.rows - 1);
+    // A chunks NA w + a: tile rows 8 (NA w + a) .. + 7
+    const uint16_t* ag[NA];
+#pragma unroll
+    for (int a = 0; a < NA; ++a) {
+        const int c = NA * w + a;
+        const int r = min(8 * c + (lane >> 3), ti.rows - 1);
         long long src = ti.row0 + r;
         if (p.a_rows) src = min(max((long long)p.a_rows[src], 0LL), p.a_nrows - 1);
-        ag = A + src * p.lda + ((w & 1) ? kcg1 : kcg0);
+        ag[a] = A + src * p.lda + ((c & 1) ? kcg1 : kcg0);
     }
     // B chunks 8 w + i: tile rows 64 w + 8 i .. + 7
     const uint16_t* bg[8];
@@ -1257,10 +1266,10 @@ __device__ __forceinline__ void gemm_tile_dec(const GemmParams& p, const TileInf
             const int nbl = p.N / 32 - 1, j = i >> 2;
             int nb;
             if (MODE == GM_UP_SWIGLU) {
-                const int t = min(ti.nt * (DBN / 64) + w, nbl);
+                const int t = min(ti.nt * (TN / 64) + w, nbl);
                 nb = j ? p.up_off / 32 + t : t;
             } else {
-                nb = min(ti.nt * (DBN / 32) + 2 * w + j, nbl);
+                nb = min(ti.nt * (TN / 32) + 2 * w + j, nbl);
             }
             bg[i] = Bg + (((size_t)nb * (p.K / 16) + (i & 3)) * 64 + lane) * 8;
             continue;
@@ -1268,10 +1277,10 @@ __device__ __forceinline__ void gemm_tile_dec(const GemmParams& p, const TileInf
         int wr;
         if (MODE == GM_UP_SWIGLU) {
             const int t = 32 * w + 8 * (i & 3) + (lane >> 3);
-            const int n = min(ti.nt * (DBN / 2) + t, p.N - 1);
+            const int n = min(ti.nt * (TN / 2) + t, p.N - 1);
             wr = i < 4 ? n : p.up_off + n;
         } else {
-            wr = min(ti.nt * DBN + 64 * w + 8 * i + (lane >> 3), p.N - 1);
+            wr = min(ti.nt * TN + 64 * w + 8 * i + (lane >> 3), p.N - 1);
         }
         bg[i] = Bg + (size_t)wr * p.ldb + ((i & 1) ? kcg1 : kcg0);
     }
@@ -1281,8 +1290,9 @@ __device__ __forceinline__ void gemm_tile_dec(const GemmParams& p, const TileInf
         const int seg = k / p.Kseg;
         // packed: a 64-wide k-tile is four consecutive 1 KB fragments (2048 elements) per row block
         const long long bo = PK ? (long long)k * 32 : (long long)seg * p.sB_seg + (k - seg * p.Kseg);
-        unsigned char* st = smem + (kt % DSTAGES) * kDStage;
-        dma16(ag + k, st + w * 1024);
+        unsigned char* st = smem + (kt % STG) * STAGE;
+#pragma unroll
+        for (int a = 0; a < NA; ++a) dma16(ag[a] + k, st + (NA * w + a) * 1024);
 #pragma unroll
         for (int i = 0; i < 8; ++i) dma16(bg[i] + bo, st + kDTileA + (8 * w + i) * 1024);
     };
@@ -1294,19 +1304,18 @@ __device__ __forceinline__ void gemm_tile_dec(const GemmParams& p, const TileInf
         acc1[q] = 0.f;
     }
     __syncthreads();   // the previous tile's epilogue may still read the LDS staging area
-    issue(0);
-    issue(1);
-    issue(2);
+#pragma unroll
+    for (int u = 0; u < STG - 1; ++u) issue(u);
     for (int kt = 0; kt < nk; ++kt) {
-        // this wave's loads of k-tile kt have landed once at most the two newer k-tiles (9 loads
-        // each) are outstanding; the barrier then covers every wave's loads and every wave's reads
-        // of the stage k-step kt-1 used, which the next issue overwrites
+        // this wave's loads of k-tile kt have landed once at most the STG - 2 newer k-tiles (NA + 8
+        // loads each) are outstanding; the barrier then covers every wave's loads and every wave's
+        // reads of the stage k-step kt-1 used, which the next issue overwrites
         asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_waitcnt(waitcnt_imm(18, 0));
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm((STG - 2) * (NA + 8), 0));
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        issue(kt + 3);
-        const unsigned char* sa = smem + (kt % DSTAGES) * kDStage;
+        issue(kt + STG - 1);
+        const unsigned char* sa = smem + (kt % STG) * STAGE;
         const unsigned char* sb = sa + kDTileA;
 #pragma unroll
         for (int s = 0; s < BK / 16; ++s) {
@@ -1338,9 +1347,9 @@ __device__ __forceinline__ void gemm_tile_dec(const GemmParams& p, const TileInf
         }
     }
     __syncthreads();
-    constexpr int OUTW = MODE == GM_UP_SWIGLU ? DBN / 2 : DBN;
-    constexpr int TPR = OUTW / 8;    // threads per row
-    constexpr int RPP = 256 / TPR;   // rows per pass
+    constexpr int OUTW = MODE == GM_UP_SWIGLU ? TN / 2 : TN;
+    constexpr int TPR = OUTW / 8;       // threads per row
+    constexpr int RPP = 64 * W / TPR;   // rows per pass
     const int cq = (tid % TPR) * 8;
     const int col0 = ti.nt * OUTW + cq;
     if (col0 >= p.N) return;
@@ -1354,10 +1363,12 @@ __device__ __forceinline__ void gemm_tile_dec(const GemmParams& p, const TileInf
 
 // Grouped: tiles over the 32-row tile prefix; dense (a few tokens through the shared experts): every
 // group covers rows [0, M_dense) in 32-row tiles.
-template <int MODE, bool GROUPED, bool PK = false>
-__global__ __launch_bounds__(256, 1) void k_gemm_bf16_dec(GemmParams p, int NT) {
+template <int MODE, bool GROUPED, bool PK = false, int W = 4>
+__global__ __launch_bounds__(64 * W) void k_gemm_bf16_dec(GemmParams p, int NT) {
     if (GROUPED != (p.offsets != nullptr)) return;  // launched with the matching instantiation only
-    __shared__ __attribute__((aligned(16))) unsigned char smem[kDSmem];
+    constexpr int SMEM = DSTAGES * (kDTileA + 64 * W * BK * 2);
+    static_assert(DBM * DEPW * 4 <= SMEM, "decode epilogue staging must fit");
+    __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
     const int nmd = (p.M_dense + DBM - 1) / DBM;     // dense: m-tiles per group
     const int total = GROUPED ? p.tiles32[p.G] * NT : p.G * nmd * NT;
     const int xcd = blockIdx.x & 7, loc = blockIdx.x >> 3, per_xcd = gridDim.x >> 3;
@@ -1386,7 +1397,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_dec(GemmParams p, int NT) 
             ti.row0 = ml * DBM;
             ti.rows = min(DBM, p.M_dense - ti.row0);
         }
-        gemm_tile_dec<MODE, PK>(p, ti, smem);
+        gemm_tile_dec<MODE, PK, W>(p, ti, smem);
     }
 }
 
@@ -1570,6 +1581,18 @@ hipError_t launch_gemm(int dtype, int mode, const GemmParams& p_in, hipStream_t 
         if (p.offsets) hipLaunchKernelGGL((k_gemm_bf16_dec<M, true>), grid, dim3(256), 0, s, p, NTd); \
         else hipLaunchKernelGGL((k_gemm_bf16_dec<M, false>), grid, dim3(256), 0, s, p, NTd);    \
     } while (0)
+        if (dec_dense && mtd * NTd < cus) {
+            // few rows and few 256-wide tiles: one-wave workgroups of 64 weight rows, several per CU
+            const int NT1 = mode == GM_UP_SWIGLU ? (p.N + 31) / 32 : (p.N + 63) / 64;
+            long long nb1 = mtd * NT1;
+            nb1 = nb1 < 3 * cus ? nb1 : 3 * cus;   // three 48 KB workgroups per CU
+            const dim3 grid1((unsigned)((nb1 + 7) / 8 * 8));
+            if (mode == GM_UP_SWIGLU) hipLaunchKernelGGL((k_gemm_bf16_dec<GM_UP_SWIGLU, false, false, 1>), grid1, dim3(64), 0, s, p, NT1);
+            else if (mode == GM_UP_RELU) hipLaunchKernelGGL((k_gemm_bf16_dec<GM_UP_RELU, false, false, 1>), grid1, dim3(64), 0, s, p, NT1);
+            else if (mode == GM_DOWN) hipLaunchKernelGGL((k_gemm_bf16_dec<GM_DOWN, false, false, 1>), grid1, dim3(64), 0, s, p, NT1);
+            else hipLaunchKernelGGL((k_gemm_bf16_dec<GM_DOWN_COMBINE, false, false, 1>), grid1, dim3(64), 0, s, p, NT1);
+            return hipGetLastError();
+        }
         if (mode == GM_UP_SWIGLU) MOE_LAUNCH_D(GM_UP_SWIGLU);
         else if (mode == GM_UP_RELU) MOE_LAUNCH_D(GM_UP_RELU);
         else if (mode == GM_DOWN) MOE_LAUNCH_D(GM_DOWN);
