@@ -289,7 +289,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const TileInfo& t
 
     // DMA assignment: wave w moves 1 KB chunks c = 4 w + i (i < 4) of each operand tile; chunk c
     // is rows 8c .. 8c+7; lane l of it is row 8c + l/8, LDS slot l%8, global chunk (l%8) ^ ((row>>1)&7).
-    const uint16_t* A = (const uint16_t*)p.A;
+    const uint16_t* A = (const uint16_t*)p.A + (p.offsets ? 0 : (size_t)ti.g * p.sA_group);
     const uint16_t* Bg = (const uint16_t*)p.B + (size_t)ti.g * p.sB_group;
     const uint16_t* ag[4];
     const uint16_t* bg[4];
@@ -483,7 +483,7 @@ __device__ __forceinline__ void gemm_tile_wide8(const GemmParams& p, const TileI
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;   // w < 8
 
-    const uint16_t* A = (const uint16_t*)p.A;
+    const uint16_t* A = (const uint16_t*)p.A + (p.offsets ? 0 : (size_t)ti.g * p.sA_group);
     const uint16_t* Bg = (const uint16_t*)p.B + (size_t)ti.g * p.sB_group;
     // A: 16 chunks, wave w moves chunks 2w, 2w+1 (rows 16 w + 8 i + lane/8)
     const uint16_t* ag[2];
@@ -746,7 +746,8 @@ __device__ __forceinline__ void gemm_tile_w4(const GemmParams& p, const TileInfo
         const int r = min(row, ti.rows - 1);
         long long src = ti.row0 + r;
         if (p.a_rows) src = min(max((long long)p.a_rows[src], 0LL), p.a_nrows - 1);
-        voA[i] = row < ti.rows ? (unsigned)(src * p.lda + ((i & 1) ? kcg1 : kcg0)) * 2u : kZeroRow;   // padding: zeros
+        const long long ga = p.offsets ? 0 : (long long)ti.g * p.sA_group;   // dense group's A offset
+        voA[i] = row < ti.rows ? (unsigned)(src * p.lda + ga + ((i & 1) ? kcg1 : kcg0)) * 2u : kZeroRow;   // padding: zeros
     }
     unsigned voB[16];   // byte offset of B chunk 16w + i of this lane within the group's weights
     {

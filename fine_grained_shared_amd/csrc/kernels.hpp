@@ -10,9 +10,13 @@ namespace moe {
 // logits [T, N] fp32 = u [T, H] . centroids [N, H]^T
 hipError_t launch_logits(int dtype, const void* u, const void* e, float* logits, int T, int H, int N,
                          hipStream_t s);
+// The prefill logits GEMM splits the reduction in two halves (two groups of K/2, written side by side as
+// [T, 2N]) when T is large: the narrow GEMM then has twice the tiles.  k_select adds the halves (first + second).
+bool logits_split(int dtype, int T, int H, int N);
 // per-token scores, selection and gate weights from the logits
 struct SelectArgs {
-    const float* logits;
+    const float* logits;      // [T, N], or [T, 2N] halves when split
+    int split;
     const float* bias;
     int T, N, K;
     int gating;
@@ -41,6 +45,7 @@ struct GemmParams {
     const void* A;            // activation rows
     long long lda;            // elements per A row
     const int32_t* a_rows;    // row-space row -> A row (NULL: identity)
+    long long sA_group;       // dense mode: group g reads A + g * sA_group (split reduction; else 0)
     long long a_nrows;        // rows of A (gathered indices are clamped into range)
     const void* B;            // weight bank base
     long long sB_group;       // elements between groups in the bank

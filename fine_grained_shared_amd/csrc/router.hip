@@ -124,6 +124,12 @@ __global__ __launch_bounds__(256) void k_logits_f32(const float* __restrict__ u,
     logits[idx] = acc;
 }
 
+// Below 32768 tokens the 128 x 128 tiles of the logits GEMM (T / 128 x N / 128 of them) leave half of
+// its two-workgroups-per-CU slots empty; two reduction halves fill them.
+bool logits_split(int dtype, int T, int H, int N) {
+    return dtype != 0 && T >= 1024 && T < 32768 && N % 64 == 0 && H % 128 == 0;
+}
+
 hipError_t launch_logits(int dtype, const void* u, const void* e, float* logits, int T, int H, int N,
                          hipStream_t s) {
     if (T == 0 || N == 0) return hipSuccess;
@@ -132,21 +138,26 @@ hipError_t launch_logits(int dtype, const void* u, const void* e, float* logits,
         hipLaunchKernelGGL(k_logits_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, (const float*)u,
                            (const float*)e, logits, T, H, N);
     } else if (T >= 1024 && N % 64 == 0) {
-        // prefill: the tiled MFMA GEMM (LDS-staged, fp32 output) over u [T, H] x e [N, H]^T
+        // prefill: the tiled MFMA GEMM (LDS-staged, fp32 output) over u [T, H] x e [N, H]^T; split, the
+        // two halves of H are two dense groups writing [T, 2N] side by side
+        const bool split = logits_split(dtype, T, H, N);
         GemmParams p{};
         p.A = u;
         p.lda = H;
         p.a_nrows = T;
         p.B = e;
         p.ldb = H;
-        p.K = H;
-        p.Kseg = H;
+        p.K = split ? H / 2 : H;
+        p.Kseg = p.K;
+        p.sA_group = split ? H / 2 : 0;
+        p.sB_group = split ? H / 2 : 0;
         p.N = N;
         p.M_dense = T;
-        p.G = 1;
+        p.G = split ? 2 : 1;
         p.max_rows = T;
         p.C = logits;
-        p.ldc = N;
+        p.ldc = split ? 2 * N : N;
+        p.sC_group = N;
         return launch_gemm(1, GM_F32OUT, p, s);
     } else if (T < 1024) {
         // one kernel (one summation order) for every T below the GEMM path, so a token's logits do
@@ -221,7 +232,9 @@ __global__ __launch_bounds__(256) void k_select(SelectArgs a) {
     for (int j = 0; j < NPL; ++j) {
         const int i = lane + 64 * j;
         const bool v = i < N;
-        l[j] = v ? a.logits[(size_t)t * N + i] : -INFINITY;
+        l[j] = !v ? -INFINITY
+                  : a.split ? a.logits[(size_t)t * 2 * N + i] + a.logits[(size_t)t * 2 * N + N + i]
+                            : a.logits[(size_t)t * N + i];
         avail |= (v ? 1u : 0u) << j;
     }
     float lmax = -INFINITY;
