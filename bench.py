@@ -326,8 +326,11 @@ def main():
     gen_s = time.time() - t0
     d = _upload(inp)
     flags = 0
+    unpacked = None
     if args.weights == "packed":
-        # a storage layout of the same weights, made once when they are loaded (not part of a step)
+        # a storage layout of the same weights, made once when they are loaded (not part of a step);
+        # the [out, in] banks are kept to time the same step on them as well
+        unpacked = {k: d[k] for k in ("w1", "w2")}
         for k in ("w1", "w2"):
             d[k] = moe.pack_weights(d[k])
         flags = moe.MOE_FLAG_PACKED_WEIGHTS
@@ -391,6 +394,18 @@ def main():
         "load": {"touched": int((counts > 0).sum()), "empty": int((counts == 0).sum()),
                  "max_over_mean": round(float(counts.max() / counts.mean()), 2)},
     }
+
+    if unpacked is not None:
+        def ustep():
+            moe.moe_layer_forward(shape, d["u"], d["centroids"], d["bias"], unpacked["w1"], d["b1"], unpacked["w2"],
+                                  d["w1_sh"], d["b1_sh"], d["w2_sh"], 0, out, idx, wts, ws)
+
+        ums = _time_steps(ustep, max(5, args.steps // 2), args.warmup)
+        result["unpacked_weights"] = {"ms_per_step": round(ums, 4), "value": round(w.T / (ums * 1e-3), 1),
+                                      "note": "the same step on the [out, in] routed banks (bit-identical output)"}
+        print("[bench] prefill, [out, in] routed banks: %.3f ms/step" % ums, file=sys.stderr, flush=True)
+        del unpacked
+        torch.cuda.empty_cache()
 
     if not args.no_decode:
         Td = args.decode_tokens
