@@ -118,13 +118,12 @@ def _short(name):
     return n.replace("void ", "").replace("moe::", "")
 
 
-def rocprof_summary(trace_dir, fetch_dir=None, write_dir=None, out_json=None):
+def rocprof_summary(trace_dir, fetch_dir=None, write_dir=None, out_json=None, dom_name=DOMINANT_KERNELS[1]):
     """Markdown summary of a rocprofv3 --kernel-trace --stats run (and optional FETCH_SIZE /
-    WRITE_SIZE passes) for the profiles/ folder."""
+    WRITE_SIZE passes) for the profiles/ folder; dom_name is the dominant kernel of the profiled run."""
     lines = []
     stats = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)
     dom = None
-    dom_name = DOMINANT_KERNELS[0]
     for f in stats:
         with open(f) as fh:
             rows = list(csv.DictReader(fh))
@@ -135,9 +134,8 @@ def rocprof_summary(trace_dir, fetch_dir=None, write_dir=None, out_json=None):
             avg = float(r["AverageNs"]) / 1e6
             lines.append("| %s | %s | %.4f | %.3f | %.1f |" % (nm, r["Calls"], avg, float(r["TotalDurationNs"]) / 1e6,
                                                               float(r["Percentage"])))
-            for cand in DOMINANT_KERNELS:
-                if nm.endswith(cand):
-                    dom, dom_name = avg, cand
+            if nm.endswith(dom_name):
+                dom = avg
     res = {"dominant_kernel": dom_name, "avg_ms": dom}
     if fetch_dir and write_dir:
         fc, wc = _read_counters(fetch_dir), _read_counters(write_dir)
@@ -296,6 +294,8 @@ def main():
     ap.add_argument("--decode-tokens", type=int, default=128)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-unpacked", action="store_true",
+                    help="with packed weights, skip timing the same step on the [out, in] banks")
     ap.add_argument("--rocprof-summary", metavar="TRACE_DIR", help="summarise a rocprofv3 run and exit")
     ap.add_argument("--pmc-fetch", metavar="DIR")
     ap.add_argument("--pmc-write", metavar="DIR")
@@ -306,7 +306,8 @@ def main():
                          "layout")
     args = ap.parse_args()
     if args.rocprof_summary:
-        text, _ = rocprof_summary(args.rocprof_summary, args.pmc_fetch, args.pmc_write, args.traffic_json)
+        text, _ = rocprof_summary(args.rocprof_summary, args.pmc_fetch, args.pmc_write, args.traffic_json,
+                                  dominant_kernel(args.weights == "packed"))
         print(text)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -330,7 +331,7 @@ def main():
     if args.weights == "packed":
         # a storage layout of the same weights, made once when they are loaded (not part of a step);
         # the [out, in] banks are kept to time the same step on them as well
-        unpacked = {k: d[k] for k in ("w1", "w2")}
+        unpacked = None if args.no_unpacked else {k: d[k] for k in ("w1", "w2")}
         for k in ("w1", "w2"):
             d[k] = moe.pack_weights(d[k])
         flags = moe.MOE_FLAG_PACKED_WEIGHTS
