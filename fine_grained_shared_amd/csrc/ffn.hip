@@ -167,6 +167,11 @@ constexpr int EPW = BN + 4;                               // fp32 staging row (f
 constexpr int kTileBytes = BM * BK * 2;                   // one operand tile (16 KB)
 constexpr int kStageBytes = 2 * kTileBytes;               // A + B
 constexpr int kSmemBytes = BM * EPW * 4 > 2 * kStageBytes ? BM * EPW * 4 : 2 * kStageBytes;
+// Fused combine: the routed-row indices and gate weights of a tile's rows, read into LDS behind the
+// staging area when the tile starts (up to kCombKmax per row; two workgroups still fit a CU).
+constexpr int kCombKmax = 12;
+constexpr int kCombBytes = BM * kCombKmax * 8;
+static_assert(2 * (kSmemBytes + kCombBytes) <= 160 * 1024, "two workgroups per CU");
 static_assert(BM == BN && BM == 128 && BK == 64, "tile layout assumes 128 x 128 x 64");
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -282,6 +287,53 @@ __device__ __forceinline__ void epilogue_row(const GemmParams& p, const TileInfo
     *reinterpret_cast<uint4*>(C + row * p.ldc + coff + col0) = pack8_bf16(v);
 }
 
+// Fused combine of two output rows a, b (tile-local ra, rb) on the 8 columns from col0, with the pair
+// rows and gates of the tile's rows in LDS (si, sg: K_r per row): the same fixed fp32 order as
+// epilogue_row (residual + shared experts, then the routed rows k = 0 .. K_r-1), one bf16 rounding.
+__device__ __forceinline__ void combine_rows(const GemmParams& p, const TileInfo& ti, float (&va)[8], float (&vb)[8],
+                                             int ra, int rb, int col0, const int32_t* si, const float* sg) {
+    const long long rowa = ti.row0 + ra, rowb = ti.row0 + rb;
+    const uint16_t* Y = (const uint16_t*)p.y_perm;
+    if (p.resid) {
+        const uint4 qa = *reinterpret_cast<const uint4*>((const uint16_t*)p.resid + rowa * p.N + col0);
+        const uint4 qb = *reinterpret_cast<const uint4*>((const uint16_t*)p.resid + rowb * p.N + col0);
+        float ua[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, ub[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        add8_bf16(ua, qa);
+        add8_bf16(ub, qb);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            va[e] = ua[e] + va[e];
+            vb[e] = ub[e] + vb[e];
+        }
+    }
+    const int K = p.K_r;
+    for (int k = 0; k < K; k += 4) {
+        uint4 ya[4], yb[4];
+        float ga[4], gb[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int kk = k + e < K ? k + e : K - 1;
+            long long xa = (long long)(uint32_t)si[ra * K + kk], xb = (long long)(uint32_t)si[rb * K + kk];
+            xa = xa < p.R ? xa : p.R - 1;
+            xb = xb < p.R ? xb : p.R - 1;
+            ga[e] = sg[ra * K + kk];
+            gb[e] = sg[rb * K + kk];
+            ya[e] = *reinterpret_cast<const uint4*>(Y + xa * p.N + col0);
+            yb[e] = *reinterpret_cast<const uint4*>(Y + xb * p.N + col0);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if (k + e < K) {
+                fma8_bf16(va, ga[e], ya[e]);
+                fma8_bf16(vb, gb[e], yb[e]);
+            }
+        }
+    }
+    uint16_t* C = (uint16_t*)p.C;
+    *reinterpret_cast<uint4*>(C + rowa * p.ldc + col0) = pack8_bf16(va);
+    if (rb != ra) *reinterpret_cast<uint4*>(C + rowb * p.ldc + col0) = pack8_bf16(vb);
+}
+
 template <int MODE>
 __device__ __forceinline__ void gemm_tile(const GemmParams& p, const TileInfo& ti, unsigned char* smem) {
     const int tid = threadIdx.x;
@@ -338,6 +390,33 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const TileInfo& t
 
     __syncthreads();  // the previous tile's epilogue may still read the LDS staging area
     issue(0, 0);
+    const bool comb_lds = MODE == GM_DOWN_COMBINE && p.K_r <= kCombKmax;
+    if (comb_lds) {
+        // this tile's pair rows and gates (rows * K_r contiguous values each), behind k-tile 0's loads
+        int32_t* si = reinterpret_cast<int32_t*>(smem + kSmemBytes);
+        float* sg = reinterpret_cast<float*>(smem + kSmemBytes + BM * kCombKmax * 4);
+        const int n = ti.rows * p.K_r;
+        const int32_t* pr = p.pair_row + (long long)ti.row0 * p.K_r;
+        const float* gw = p.topk_w + (long long)ti.row0 * p.K_r;
+        int32_t xi[kCombKmax * BM / 256];
+        float xg[kCombKmax * BM / 256];
+#pragma unroll
+        for (int j = 0; j < kCombKmax * BM / 256; ++j) {
+            const int o = tid + 256 * j;
+            if (o < n) {
+                xi[j] = pr[o];
+                xg[j] = gw[o];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < kCombKmax * BM / 256; ++j) {
+            const int o = tid + 256 * j;
+            if (o < n) {
+                si[o] = xi[j];
+                sg[o] = xg[j];
+            }
+        }
+    }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (int kt = 0; kt < nk; ++kt) {
@@ -372,6 +451,27 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const TileInfo& t
     const int cq = (tid % TPR) * 8;
     const int col0 = ti.nt * OUTW + cq;
     if (col0 >= p.N) return;
+    if (MODE == GM_DOWN_COMBINE && comb_lds) {
+        // two rows per pass: their residual and routed-row loads are all in flight together
+        const int32_t* si = reinterpret_cast<const int32_t*>(smem + kSmemBytes);
+        const float* sg = reinterpret_cast<const float*>(smem + kSmemBytes + BM * kCombKmax * 4);
+        for (int rl = tid / TPR; rl < ti.rows; rl += 2 * RPP) {
+            const int rb = rl + RPP < ti.rows ? rl + RPP : rl;   // a lone last row is done twice (same values)
+            float va[8], vb[8];
+            {
+                const float4 a0 = *reinterpret_cast<const float4*>(&st[rl * EPW + cq]);
+                const float4 a1 = *reinterpret_cast<const float4*>(&st[rl * EPW + cq + 4]);
+                const float4 b0 = *reinterpret_cast<const float4*>(&st[rb * EPW + cq]);
+                const float4 b1 = *reinterpret_cast<const float4*>(&st[rb * EPW + cq + 4]);
+                va[0] = a0.x; va[1] = a0.y; va[2] = a0.z; va[3] = a0.w;
+                va[4] = a1.x; va[5] = a1.y; va[6] = a1.z; va[7] = a1.w;
+                vb[0] = b0.x; vb[1] = b0.y; vb[2] = b0.z; vb[3] = b0.w;
+                vb[4] = b1.x; vb[5] = b1.y; vb[6] = b1.z; vb[7] = b1.w;
+            }
+            combine_rows(p, ti, va, vb, rl, rb, col0, si, sg);
+        }
+        return;
+    }
     for (int rl = tid / TPR; rl < ti.rows; rl += RPP) {
         const float4 v0 = *reinterpret_cast<const float4*>(&st[rl * EPW + cq]);
         const float4 v1 = *reinterpret_cast<const float4*>(&st[rl * EPW + cq + 4]);
@@ -388,7 +488,7 @@ __device__ __forceinline__ int total_tiles(const GemmParams& p, int NT) {
 template <int MODE, bool GROUPED>
 __global__ __launch_bounds__(256, 2) void k_gemm_bf16(GemmParams p, int NT) {
     if (GROUPED != (p.offsets != nullptr)) return;  // launched with the matching instantiation only
-    __shared__ __attribute__((aligned(16))) unsigned char smem[kSmemBytes];
+    __shared__ __attribute__((aligned(16))) unsigned char smem[kSmemBytes + (MODE == GM_DOWN_COMBINE ? kCombBytes : 0)];
     const int total = total_tiles(p, NT);
     const int xcd = blockIdx.x & 7, loc = blockIdx.x >> 3, per_xcd = gridDim.x >> 3;
     const int beg = (int)((long long)total * xcd / 8);
