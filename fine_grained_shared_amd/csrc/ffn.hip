@@ -1086,13 +1086,23 @@ hipError_t launch_pack_b(const void* w, void* out, int G, int N, int K, hipStrea
 // blocks 1-3.  That is 20 vector-memory operations per k-step.
 constexpr int kPStage = BM * BK * 2;   // 16 KB A stage
 constexpr int kPStages = 4;
+// NJ = 32-column weight blocks per wave: 4 (128 x 512 tile, one workgroup per CU) or 2 (128 x 256
+// tile, two workgroups per CU, so that one's prologue and epilogue overlap the other's MFMAs).  A
+// k-step issues 4 A loads and 4 NJ B loads.
 // The A loads of k-tile kt+1 (issued in k-step kt-3, or in the prologue) must have landed when k-step
 // kt starts reading them (chunk 3).  At that point at most this many vector-memory operations were
-// issued after them: 52 in k-step 0 (prologue order: A0..A3, B0, B1), 55 in the steady state.
-constexpr int kPWaitA = 52;
-// prologue: A(0) has A1..A3 (12) and B0, B1 (32) issued after it
-constexpr int kPWaitA0 = 44;
-static_assert(kPStages * kPStage <= kWSmem, "A ring must fit");
+// issued after them: 11 NJ + 8 in k-step 0 (prologue order: A0..A3, B0, B1, then three chunks of
+// B loads), 12 NJ + 7 in the steady state (NJ = 4: 52 and 55).
+__host__ __device__ constexpr int p_wait_a(int nj) { return 11 * nj + 8; }
+// prologue: A(0) has A1..A3 (12) and B0, B1 (8 NJ) issued after it
+__host__ __device__ constexpr int p_wait_a0(int nj) { return 8 * nj + 12; }
+// LDS of a packed-kernel workgroup: the A ring, reused for the bf16 staging of the output tile
+__host__ __device__ constexpr int p_out_cols(int mode, int nj) { return mode == GM_UP_SWIGLU ? 64 * nj : 128 * nj; }
+__host__ __device__ constexpr int p_smem(int mode, int nj) {
+    return kPStages * kPStage > BM / 2 * (p_out_cols(mode, nj) + 16) * 4 ? kPStages * kPStage
+                                                                          : BM / 2 * (p_out_cols(mode, nj) + 16) * 4;
+}
+static_assert(p_smem(GM_DOWN, 4) <= kWSmem && 2 * p_smem(GM_DOWN, 2) <= kWSmem, "A ring and staging must fit");
 
 // Epilogue of the packed kernel (grouped bf16 modes: SwiGLU, ReLU, down).  Each lane holds, for every
 // 32 x 32 accumulator block, rows 8 (q / 4) + 4 (lane / 32) + q % 4 of column lane % 32; the values are
@@ -1101,22 +1111,22 @@ static_assert(kPStages * kPStage <= kWSmem, "A ring must fit");
 // word [row pair][column].  Threads then read the words of 8 columns of a row pair, separate the two
 // rows with byte permutes and store 16 bytes per row.  Row pairs are padded by 16 words, so the two
 // half-waves of a staging write fall in disjoint LDS banks.
-template <int MODE>
-__device__ __forceinline__ void w4p_epilogue(const GemmParams& p, const TileInfo& ti, f32x16 (&acc)[4][4],
+template <int MODE, int NJ>
+__device__ __forceinline__ void w4p_epilogue(const GemmParams& p, const TileInfo& ti, f32x16 (&acc)[4][NJ],
                                              unsigned char* smem) {
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));   // lane values recomputed here, not kept live across the k-loop
     const int lane = tid & 63, w = tid >> 6;
-    constexpr int OUTW = MODE == GM_UP_SWIGLU ? 256 : WBN;   // output columns of the tile
+    constexpr int OUTW = p_out_cols(MODE, NJ);                // output columns of the tile
     constexpr int SW = OUTW + 16;                            // staged words per row pair
-    constexpr int NJ = MODE == GM_UP_SWIGLU ? 2 : 4;         // output column blocks per wave
-    static_assert(BM / 2 * SW * 4 <= kWSmem, "bf16 staging must fit");
+    constexpr int NJO = MODE == GM_UP_SWIGLU ? NJ / 2 : NJ;   // output column blocks per wave
+    static_assert(BM / 2 * SW * 4 <= p_smem(MODE, NJ), "bf16 staging must fit");
     uint32_t* st = reinterpret_cast<uint32_t*>(smem);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int jb = 0; jb < NJ; ++jb) {
-            const int cl = (MODE == GM_UP_SWIGLU ? 64 * w : 128 * w) + 32 * jb + (lane & 31);   // tile column
+        for (int jb = 0; jb < NJO; ++jb) {
+            const int cl = 32 * NJO * w + 32 * jb + (lane & 31);   // tile column
             float bias = 0.f;
             if (MODE == GM_UP_RELU && p.bias) {
                 const int col = min(ti.nt * OUTW + cl, p.N - 1);
@@ -1129,8 +1139,8 @@ __device__ __forceinline__ void w4p_epilogue(const GemmParams& p, const TileInfo
                     const int q = 4 * a + b;
                     float x0, x1;
                     if (MODE == GM_UP_SWIGLU) {
-                        x0 = silu(acc[i][jb][q]) * acc[i][jb + 2][q];
-                        x1 = silu(acc[i][jb][q + 1]) * acc[i][jb + 2][q + 1];
+                        x0 = silu(acc[i][jb][q]) * acc[i][jb + NJO][q];
+                        x1 = silu(acc[i][jb][q + 1]) * acc[i][jb + NJO][q + 1];
                     } else if (MODE == GM_UP_RELU) {
                         x0 = fmaxf(acc[i][jb][q] + bias, 0.0f);
                         x1 = fmaxf(acc[i][jb][q + 1] + bias, 0.0f);
@@ -1171,7 +1181,7 @@ __device__ __forceinline__ void w4p_epilogue(const GemmParams& p, const TileInfo
 // counts such a load as a possible LDS access as well, and then waits for every outstanding load
 // (vmcnt(0)) before the next use of a loaded register: correct, but the B prefetch no longer
 // overlaps.  Otherwise A uses buffer loads into LDS with 32-bit offsets, which keep the counts exact.
-template <int MODE, bool A_FLAT>
+template <int MODE, bool A_FLAT, int NJ>
 __device__ __forceinline__ void gemm_tile_w4p(const GemmParams& p, const TileInfo& ti, unsigned char* smem) {
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));   // per-tile lane values: not hoisted out of the tile loop
@@ -1181,17 +1191,17 @@ __device__ __forceinline__ void gemm_tile_w4p(const GemmParams& p, const TileInf
 
     // B: the group's packed matrix; fragment (nb, kc) of this lane at (nb * kcn + kc) * 1024 + 16 lane
     const __amdgpu_buffer_rsrc_t rsB = make_rsrc((const uint16_t*)p.B + (size_t)ti.g * p.sB_group, p.b_bytes);
-    unsigned voB[4];
+    unsigned voB[NJ];
     {
         const int nbl = p.N / 32 - 1;   // last row block of the output columns
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < NJ; ++j) {
             int nb;
-            if (MODE == GM_UP_SWIGLU) {
-                const int t = min(ti.nt * 8 + 2 * w + (j & 1), nbl);
-                nb = j < 2 ? t : p.up_off / 32 + t;
+            if (MODE == GM_UP_SWIGLU) {   // gate blocks j < NJ / 2, the matching up blocks after them
+                const int t = min(ti.nt * 2 * NJ + NJ / 2 * w + j % (NJ / 2), nbl);
+                nb = j < NJ / 2 ? t : p.up_off / 32 + t;
             } else {
-                nb = min(ti.nt * 16 + 4 * w + j, nbl);
+                nb = min(ti.nt * 4 * NJ + NJ * w + j, nbl);
             }
             voB[j] = (unsigned)nb * kcn * 1024u + (unsigned)lane * 16u;
         }
@@ -1222,15 +1232,15 @@ __device__ __forceinline__ void gemm_tile_w4p(const GemmParams& p, const TileInf
         else __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, (lds_ptr_t)dst, 16, voA[i] | zero, 2 * k, 0, 0);
     };
 
-    f32x16 acc[4][4];
+    f32x16 acc[4][NJ];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < NJ; ++j)
 #pragma unroll
             for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
     bf16x8 af[2][4];
-    v4u bq[2][4][4];   // [k-step parity][chunk][row block]
+    v4u bq[2][4][NJ];   // [k-step parity][chunk][row block]
 
     __syncthreads();   // the previous tile's epilogue may still read the LDS staging area
 #pragma unroll
@@ -1244,11 +1254,11 @@ __device__ __forceinline__ void gemm_tile_w4p(const GemmParams& p, const TileInf
 #pragma unroll
         for (int s = 0; s < 4; ++s)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < NJ; ++j)
                 bq[t][s][j] = __builtin_amdgcn_raw_buffer_load_b128(rsB, voB[j] | (t < nk ? 0u : kZeroRow),
                                                                     min(t, nk - 1) * 4096 + s * 1024, 0);
     asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(waitcnt_imm(kPWaitA0, 0));
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(p_wait_a0(NJ), 0));
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
 #pragma unroll
@@ -1268,12 +1278,12 @@ __device__ __forceinline__ void gemm_tile_w4p(const GemmParams& p, const TileInf
                 // stage kt, which the A loads below refill
                 __builtin_amdgcn_sched_barrier(0);
                 asm volatile("" ::: "memory");
-                __builtin_amdgcn_s_waitcnt(waitcnt_imm(kPWaitA, 0));
+                __builtin_amdgcn_s_waitcnt(waitcnt_imm(p_wait_a(NJ), 0));
                 __builtin_amdgcn_s_barrier();
                 asm volatile("" ::: "memory");
             }
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < NJ; ++j)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     __builtin_amdgcn_sched_barrier(0);
@@ -1301,18 +1311,18 @@ __device__ __forceinline__ void gemm_tile_w4p(const GemmParams& p, const TileInf
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    w4p_epilogue<MODE>(p, ti, acc, smem);
+    w4p_epilogue<MODE, NJ>(p, ti, acc, smem);
 }
 
-template <int MODE, bool A_FLAT>
-__global__ __launch_bounds__(256, 1) void k_gemm_bf16_w4p(GemmParams p, int NT) {
-    __shared__ __attribute__((aligned(16))) unsigned char smem[kWSmem];
+template <int MODE, bool A_FLAT, int NJ = 4>
+__global__ __launch_bounds__(256, 4 / NJ) void k_gemm_bf16_w4p(GemmParams p, int NT) {
+    __shared__ __attribute__((aligned(16))) unsigned char smem[p_smem(MODE, NJ)];
     const int total = total_tiles(p, NT);
     const int xcd = blockIdx.x & 7, loc = blockIdx.x >> 3, per_xcd = gridDim.x >> 3;
     for (int L = window_tile(xcd, loc, per_xcd); L < total; L += (int)gridDim.x) {
         TileInfo ti;
         decode_tile(p, NT, BM, L, ti);
-        gemm_tile_w4p<MODE, A_FLAT>(p, ti, smem);
+        gemm_tile_w4p<MODE, A_FLAT, NJ>(p, ti, smem);
     }
 }
 
@@ -1603,15 +1613,25 @@ hipError_t launch_gemm(int dtype, int mode, const GemmParams& p_in, hipStream_t 
             else hipLaunchKernelGGL((k_gemm_bf16_dec<GM_DOWN, true, true>), grid, dim3(256), 0, s, p, NTd);
             return hipGetLastError();
         }
-        const int NTp = mode == GM_UP_SWIGLU ? (p.N + 255) / 256 : (p.N + WBN - 1) / WBN;
+        // reductions of at most 8 k-steps: 128 x 256 tiles, two workgroups per CU, so that one's prologue
+        // and epilogue (as long as its k-loop here) overlap the other's MFMAs; longer ones lose more to the
+        // doubled activation traffic than they gain
+        const int nj = p.K <= 512 ? 2 : 4;
+        const int NTp = (p.N + p_out_cols(mode, nj) - 1) / p_out_cols(mode, nj);
         const long long mtp = (p.max_rows + BM - 1) / BM + p.G;
         long long nb = (mtp * NTp + 7) / 8 * 8;
-        nb = nb < cus ? nb : cus;
+        const long long slots = nj == 2 ? 2 * cus : cus;
+        nb = nb < slots ? nb : slots;
         const dim3 grid((unsigned)((nb + 7) / 8 * 8));
-#define MOE_LAUNCH_P(M)                                                                                       \
-    do {                                                                                                      \
-        if (p.a_bytes > 0) hipLaunchKernelGGL((k_gemm_bf16_w4p<M, false>), grid, dim3(256), 0, s, p, NTp);   \
-        else hipLaunchKernelGGL((k_gemm_bf16_w4p<M, true>), grid, dim3(256), 0, s, p, NTp);                   \
+#define MOE_LAUNCH_P(M)                                                                                           \
+    do {                                                                                                          \
+        if (nj == 2) {                                                                                            \
+            if (p.a_bytes > 0) hipLaunchKernelGGL((k_gemm_bf16_w4p<M, false, 2>), grid, dim3(256), 0, s, p, NTp); \
+            else hipLaunchKernelGGL((k_gemm_bf16_w4p<M, true, 2>), grid, dim3(256), 0, s, p, NTp);               \
+        } else {                                                                                                  \
+            if (p.a_bytes > 0) hipLaunchKernelGGL((k_gemm_bf16_w4p<M, false>), grid, dim3(256), 0, s, p, NTp);   \
+            else hipLaunchKernelGGL((k_gemm_bf16_w4p<M, true>), grid, dim3(256), 0, s, p, NTp);                   \
+        }                                                                                                         \
     } while (0)
         if (mode == GM_UP_SWIGLU) MOE_LAUNCH_P(GM_UP_SWIGLU);
         else if (mode == GM_UP_RELU) MOE_LAUNCH_P(GM_UP_RELU);

@@ -3,8 +3,9 @@
 The packing kernel is checked against the layout written out on the host.  The packed layer and the
 packed expert FFN are checked against the unpacked ones bit for bit: every GEMM kernel accumulates an
 output in one fixed order, so the storage order of the weights cannot change a result.  One packed
-layer is also compared with the oracle.  The shapes cover both packed kernels (the 128 x 512 tile
-and the 32-row decode tile), odd k-step counts, ragged column tiles and empty expert groups.
+layer is also compared with the oracle.  The shapes cover the packed kernels (the 128 x 512 tile, the
+128 x 256 tile of reductions up to 512 and the 32-row decode tile), odd k-step counts, ragged column
+tiles and empty expert groups.
 """
 import gc
 
@@ -24,6 +25,8 @@ RAGGED = Workload("packed_ragged", "ragged bf16 SwiGLU sigmoid+bias layer", 600,
 
 VARIANTS = {
     "ragged": RAGGED,
+    # reductions longer than 8 k-steps (H=576: 9, I=640: 10) take the 128 x 512 tile; ragged column tiles
+    "ragged_wide": RAGGED.with_(name="packed_ragged_wide", H=576, I=640),
     "ragged_decode": RAGGED.with_(name="packed_ragged_decode", T=40),
     "relu": RAGGED.with_(name="packed_relu", gating=GATE_SOFTMAX, act=ACT_RELU_BIAS, bias_var=0.0, I=256),
     "relu_decode": RAGGED.with_(name="packed_relu_decode", gating=GATE_SOFTMAX, act=ACT_RELU_BIAS, bias_var=0.0,
