@@ -13,7 +13,7 @@ template <typename E>
 __device__ __forceinline__ void load8(const E* p, float (&v)[8]);
 template <>
 __device__ __forceinline__ void load8<uint16_t>(const uint16_t* p, float (&v)[8]) {
-    const uint4 q = *reinterpret_cast<const uint4*>(p);
+    const uint4 q = ld_once16(p);   // every input row of the combine is read once
     const uint32_t w[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
