@@ -191,28 +191,43 @@ __device__ __forceinline__ int unpack_idx(unsigned long long p) {
     return (int)(0xFFFFFFFFu - (uint32_t)(p & 0xFFFFFFFFull));
 }
 
-// One round of argmax over the entries whose bit is set in `avail` (bit j: expert lane + 64 j);
-// clears the winner's bit in its owner lane and returns the winner's index.  The winner's
-// values of v0 and v1 are broadcast into w0 and w1 (tracked alongside the key, so no
-// register array is indexed dynamically).
+// Wave-wide maximum of a 32-bit value, left in a scalar register: DPP permutes inside each row of 16
+// lanes (pairs, quads, half-rows, rows), then the four row maxima read out with readlane.  Every lane
+// of the wave must be active.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));    // quad_perm 1,0,3,2
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));    // quad_perm 2,3,0,1
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));   // row_half_mirror
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));   // row_mirror
+    const uint32_t r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
+    const uint32_t r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
+    return max(max(r0, r1), max(r2, r3));
+}
+
+// Index of the largest packed key of the wave (each lane offers its own best; 0 = nothing): the
+// largest key bits first, then, only when several lanes hold them, the largest ~index among those.
+__device__ __forceinline__ int wave_argmax(unsigned long long best) {
+    const uint32_t hi = (uint32_t)(best >> 32), lo = (uint32_t)best;
+    const uint32_t mh = wave_max_u32(hi);
+    const unsigned long long m = __ballot(hi == mh);
+    uint32_t ml;
+    if (__popcll(m) == 1) ml = __builtin_amdgcn_readlane(lo, __ffsll((long long)m) - 1);
+    else ml = wave_max_u32(hi == mh ? lo : 0u);
+    return (int)(0xFFFFFFFFu - ml);
+}
+
+// One selection round over the packed keys pk (entry j of a lane: expert lane + 64 j; 0 = taken or
+// absent): returns the winner and clears its entry.
 template <int NPL>
-__device__ __forceinline__ int take_best(const float (&key)[NPL], uint32_t& avail, int lane, const float (&v0)[NPL],
-                                         const float (&v1)[NPL], float& w0, float& w1) {
-    unsigned long long best = 0;
-    float b0 = 0.f, b1 = 0.f;
+__device__ __forceinline__ int take_best(unsigned long long (&pk)[NPL], int lane) {
+    unsigned long long b = 0;
 #pragma unroll
-    for (int j = 0; j < NPL; ++j) {
-        const unsigned long long p = ((avail >> j) & 1u) ? pack_key(key[j], lane + 64 * j) : 0ull;
-        const bool better = p > best;
-        best = better ? p : best;
-        b0 = better ? v0[j] : b0;
-        b1 = better ? v1[j] : b1;
-    }
-    best = wave_max_u64(best);
-    const int idx = unpack_idx(best);
-    if ((idx & 63) == lane) avail &= ~(1u << (idx >> 6));
-    w0 = __shfl(b0, idx & 63);
-    w1 = __shfl(b1, idx & 63);
+    for (int j = 0; j < NPL; ++j) b = pk[j] > b ? pk[j] : b;
+    const int idx = wave_argmax(b);
+    const int slot = idx >> 6;   // wave-uniform
+#pragma unroll
+    for (int j = 0; j < NPL; ++j)
+        if (j == slot && lane == (idx & 63)) pk[j] = 0;
     return idx;
 }
 
@@ -227,15 +242,12 @@ __global__ __launch_bounds__(256) void k_select(SelectArgs a) {
     const int N = a.N;
 
     float l[NPL], key[NPL], s[NPL];
-    uint32_t avail = 0;
 #pragma unroll
     for (int j = 0; j < NPL; ++j) {
         const int i = lane + 64 * j;
-        const bool v = i < N;
-        l[j] = !v ? -INFINITY
-                  : a.split ? a.logits[(size_t)t * 2 * N + i] + a.logits[(size_t)t * 2 * N + N + i]
-                            : a.logits[(size_t)t * N + i];
-        avail |= (v ? 1u : 0u) << j;
+        l[j] = i >= N ? -INFINITY
+                      : a.split ? a.logits[(size_t)t * 2 * N + i] + a.logits[(size_t)t * 2 * N + N + i]
+                                : a.logits[(size_t)t * N + i];
     }
     float lmax = -INFINITY;
 #pragma unroll
@@ -259,6 +271,9 @@ __global__ __launch_bounds__(256) void k_select(SelectArgs a) {
         }
         z = wave_sum(z);
     }
+    unsigned long long pk[NPL];
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) pk[j] = lane + 64 * j < N ? pack_key(key[j], lane + 64 * j) : 0ull;
 
     if (a.n_group > 0) {
         // group scores: sum of the keys of each contiguous group, in index order
@@ -267,30 +282,37 @@ __global__ __launch_bounds__(256) void k_select(SelectArgs a) {
         for (int j = 0; j < NPL; ++j) sh_key[wv][lane + 64 * j] = a.gating == 1 ? key[j] : s[j] / z;
         __syncthreads();
         const int per = N / a.n_group;
-        float gs = -INFINITY;
-        if (lane < a.n_group) {
-            gs = 0.f;
+        float gs = 0.f;
+        if (lane < a.n_group)
             for (int q = 0; q < per; ++q) gs += sh_key[wv][lane * per + q];
-        }
-        float gkey[1] = {gs};
-        uint32_t gav = lane < a.n_group ? 1u : 0u;
+        unsigned long long gpk[1] = {lane < a.n_group ? pack_key(gs, lane) : 0ull};
         unsigned long long chosen = 0;
-        float d0, d1;
-        for (int r = 0; r < a.topk_group; ++r) chosen |= 1ull << take_best<1>(gkey, gav, lane, gkey, gkey, d0, d1);
+        for (int r = 0; r < a.topk_group; ++r) chosen |= 1ull << take_best<1>(gpk, lane);
 #pragma unroll
         for (int j = 0; j < NPL; ++j) {
             const int i = lane + 64 * j;
-            if (!((chosen >> (i / per)) & 1ull)) avail &= ~(1u << j);
+            if (!((chosen >> (i / per)) & 1ull)) pk[j] = 0;
         }
     }
-    float wl, ws;
-    for (int r = 0; r < a.mask_r; ++r) take_best<NPL>(key, avail, lane, l, s, wl, ws);
+    for (int r = 0; r < a.mask_r; ++r) take_best<NPL>(pk, lane);
 
     int my_idx = 0;
-    float my_l = 0.f, my_s = 0.f;
     for (int k = 0; k < a.K; ++k) {
-        const int idx = take_best<NPL>(key, avail, lane, l, s, wl, ws);
-        if (lane == k) { my_idx = idx; my_l = wl; my_s = ws; }
+        const int idx = take_best<NPL>(pk, lane);
+        if (lane == k) my_idx = idx;
+    }
+    // the logit and score of this lane's pick, from its owner lane
+    float my_l = 0.f, my_s = 0.f;
+    {
+        const int src = my_idx & 63, slot = my_idx >> 6;
+#pragma unroll
+        for (int j = 0; j < NPL; ++j) {
+            const float lj = __shfl(l[j], src), sj = __shfl(s[j], src);
+            if (slot == j) {
+                my_l = lj;
+                my_s = sj;
+            }
+        }
     }
     const bool mine = lane < a.K;
     float g;
