@@ -1662,8 +1662,11 @@ hipError_t launch_gemm(int dtype, int mode, const GemmParams& p_in, hipStream_t 
     // The fused combine stays on the 128 x 128 tiles: its epilogue gathers K_r routed rows per
     // output row, and two workgroups per CU overlap that gather with the other's MFMAs.
     const bool w4 = wide_mode() == 2 && p.a_bytes > 0 && p.b_bytes > 0;
+    // fp32 output (router logits) with whole 512-wide column tiles takes it from one tile per CU on: the
+    // 128 x 128 kernel's single-stage k-loop is slower than the wide tile's at any count
     const bool wide = wide_mode() != 0 && mode != GM_DOWN_COMBINE && (w4 || mode != GM_F32OUT) &&
-                      mt * NTw >= 2 * cus && rows_per_group >= 64;
+                      (mt * NTw >= 2 * cus || (mode == GM_F32OUT && p.N % WBN == 0 && mt * NTw >= cus)) &&
+                      rows_per_group >= 64;
     if (wide) {
         // persistent grid: one workgroup per CU (the two operand stages fill the LDS)
         long long nb = (mt * NTw + 7) / 8 * 8;
