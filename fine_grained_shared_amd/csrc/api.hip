@@ -106,7 +106,7 @@ Layout layout_of(const moe_shape* s) {
     L.offsets = take(((size_t)s->N_r + 1) * 4);
     L.row_token = take(R * 4);
     L.pair_row = take(R * 4);
-    L.chunks = take(nchunk * s->N_r * 4);
+    L.chunks = take(2 * nchunk * s->N_r * 4);   // per-chunk counts, then the segment bases
     L.tiles = take(moe::kTilePlans * ((size_t)s->N_r + 1) * 4);
     L.act = take(R * s->I * E);
     L.y_perm = take(R * s->H * E);
@@ -143,8 +143,10 @@ int do_dispatch(const moe_shape* s, const int32_t* idx, int32_t* offsets, int32_
                 int32_t* chunks, hipStream_t st) {
     const int nchunk = (s->T + moe::kChunk - 1) / moe::kChunk;
     MOE_TRY(MOE_PROF_DISPATCH, st, moe::launch_count(idx, s->T, s->K_r, s->N_r, chunks, st));
-    MOE_TRY(MOE_PROF_DISPATCH, st, moe::launch_scan(chunks, s->K_r > 0 ? nchunk : 0, s->N_r, offsets, st));
-    MOE_TRY(MOE_PROF_DISPATCH, st, moe::launch_scatter(idx, s->T, s->K_r, s->N_r, chunks, row_token, pair_row, st));
+    int32_t* bases = chunks + (size_t)nchunk * s->N_r;
+    MOE_TRY(MOE_PROF_DISPATCH, st,
+            moe::launch_scan(chunks, bases, s->K_r > 0 ? nchunk : 0, s->N_r, offsets, st));
+    MOE_TRY(MOE_PROF_DISPATCH, st, moe::launch_scatter(idx, s->T, s->K_r, s->N_r, bases, row_token, pair_row, st));
     return MOE_OK;
 }
 

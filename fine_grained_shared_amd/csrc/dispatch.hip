@@ -29,23 +29,43 @@ __global__ __launch_bounds__(256) void k_count(const int32_t* __restrict__ idx, 
     for (int e = threadIdx.x; e < N; e += 256) chunk_counts[(size_t)c * N + e] = hist[e];
 }
 
-// One workgroup: column-wise exclusive prefix over chunks (in place, turned into absolute
-// segment bases), per-expert totals, and offsets = exclusive prefix of the totals.
-__global__ __launch_bounds__(1024) void k_scan(int32_t* __restrict__ cc, int nchunk, int N,
-                                               int32_t* __restrict__ offsets) {
-    __shared__ int32_t tot[1024];
+// Column-wise exclusive prefix over chunks, as absolute segment bases (bases[c][e] = offsets[e] + pairs
+// of e in chunks before c), and offsets = exclusive prefix of the per-expert totals (N <= 1024).
+// Workgroup b writes the columns of experts [64 b, 64 b + 64): its 1024 threads take 16 contiguous
+// chunk ranges of each of those experts.  Every workgroup first computes all the totals (a table of
+// nchunk x N counts, read from L2) and their prefix; workgroup 0 writes offsets.  The counts are only
+// read, so the workgroups do not race.  Integer sums: the order does not matter.
+__global__ __launch_bounds__(1024) void k_scan(const int32_t* __restrict__ cc, int32_t* __restrict__ bases,
+                                               int nchunk, int N, int32_t* __restrict__ offsets) {
+    __shared__ int32_t base[1024];      // per-expert totals, then their exclusive prefix
+    __shared__ int32_t part[16][64];    // this workgroup's experts: sums of the 16 chunk ranges
     __shared__ int32_t wsum[16];
-    const int e = threadIdx.x;
-    int run = 0;
-    if (e < N) {
-        for (int c = 0; c < nchunk; ++c) {
-            const int v = cc[(size_t)c * N + e];
-            cc[(size_t)c * N + e] = run;
-            run += v;
-        }
+    const int tid = threadIdx.x;
+    if (N <= 0) {
+        if (tid == 0 && blockIdx.x == 0) offsets[0] = 0;
+        return;
     }
-    // block-wide exclusive scan of the totals (N <= 1024)
-    const int lane = e & 63, w = e >> 6;
+    // 1. totals: thread (e, q) with e = tid % N sums chunks q, q + P, ... (P = 1024 / N of them per expert)
+    if (tid < N) base[tid] = 0;
+    __syncthreads();
+    const int P = 1024 / N;
+    if (tid < P * N) {
+        const int e = tid % N, q = tid / N;
+        int sum = 0, c = q;
+        for (; c + 7 * P < nchunk; c += 8 * P) {
+            int v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = cc[(size_t)(c + u * P) * N + e];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) sum += v[u];
+        }
+        for (; c < nchunk; c += P) sum += cc[(size_t)c * N + e];
+        atomicAdd(&base[e], sum);
+    }
+    __syncthreads();
+    // 2. exclusive prefix of the totals over the experts (thread e holds expert e)
+    const int lane = tid & 63, w = tid >> 6;
+    const int run = tid < N ? base[tid] : 0;
     int incl = run;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -54,22 +74,60 @@ __global__ __launch_bounds__(1024) void k_scan(int32_t* __restrict__ cc, int nch
     }
     if (lane == 63) wsum[w] = incl;
     __syncthreads();
-    if (e == 0) {
+    if (tid == 0) {
         int acc = 0;
         for (int q = 0; q < 16; ++q) {
             const int v = wsum[q];
             wsum[q] = acc;
             acc += v;
         }
-        tot[0] = acc;
+        if (blockIdx.x == 0) offsets[N] = acc;
     }
     __syncthreads();
     const int excl = incl - run + wsum[w];
-    if (e < N) {
-        offsets[e] = excl;
-        for (int c = 0; c < nchunk; ++c) cc[(size_t)c * N + e] += excl;
+    if (tid < N) {
+        base[tid] = excl;
+        if (blockIdx.x == 0) offsets[tid] = excl;
     }
-    if (e == 0) offsets[N] = tot[0];
+    // 3. this workgroup's experts: chunk range r of expert e = 64 b + el
+    const int el = tid & 63, r = tid >> 6;
+    const int e = blockIdx.x * 64 + el;
+    const int L = (nchunk + 15) / 16;
+    const int c0 = min(r * L, nchunk), c1 = min(c0 + L, nchunk);
+    int rsum = 0;
+    if (e < N) {
+        int c = c0;
+        for (; c + 8 <= c1; c += 8) {
+            int v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = cc[(size_t)(c + u) * N + e];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) rsum += v[u];
+        }
+        for (; c < c1; ++c) rsum += cc[(size_t)c * N + e];
+    }
+    part[r][el] = rsum;
+    __syncthreads();
+    if (e < N) {
+        int start = base[e];
+        for (int q = 0; q < r; ++q) start += part[q][el];
+        int c = c0;
+        for (; c + 8 <= c1; c += 8) {
+            int v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = cc[(size_t)(c + u) * N + e];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                bases[(size_t)(c + u) * N + e] = start;
+                start += v[u];
+            }
+        }
+        for (; c < c1; ++c) {
+            const int v = cc[(size_t)c * N + e];
+            bases[(size_t)c * N + e] = start;
+            start += v;
+        }
+    }
 }
 
 __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ idx, int T, int K, int N,
@@ -122,8 +180,10 @@ hipError_t launch_count(const int32_t* idx, int T, int K, int N, int32_t* chunk_
     return hipGetLastError();
 }
 
-hipError_t launch_scan(int32_t* chunk_counts, int nchunk, int N, int32_t* offsets, hipStream_t s) {
-    hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, chunk_counts, nchunk, N, offsets);
+hipError_t launch_scan(const int32_t* chunk_counts, int32_t* chunk_base, int nchunk, int N, int32_t* offsets,
+                       hipStream_t s) {
+    hipLaunchKernelGGL(k_scan, dim3(N > 64 ? (N + 63) / 64 : 1), dim3(1024), 0, s, chunk_counts, chunk_base, nchunk,
+                       N, offsets);
     return hipGetLastError();
 }
 

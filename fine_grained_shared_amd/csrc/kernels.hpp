@@ -29,7 +29,9 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t s);
 // ---------------------------------------------------------------- dispatch
 constexpr int kChunk = 256;  // tokens per dispatch workgroup
 hipError_t launch_count(const int32_t* idx, int T, int K, int N, int32_t* chunk_counts, hipStream_t s);
-hipError_t launch_scan(int32_t* chunk_counts, int nchunk, int N, int32_t* offsets, hipStream_t s);
+// counts [nchunk, N] -> bases [nchunk, N] (absolute start of chunk c's rows of expert e) and offsets [N + 1]
+hipError_t launch_scan(const int32_t* chunk_counts, int32_t* chunk_base, int nchunk, int N, int32_t* offsets,
+                       hipStream_t s);
 hipError_t launch_scatter(const int32_t* idx, int T, int K, int N, const int32_t* chunk_base,
                           int32_t* row_token, int32_t* pair_row, hipStream_t s);
 hipError_t launch_gather(int dtype, const void* u, const int32_t* row_token, int R, int H, void* x_perm,
