@@ -1439,16 +1439,24 @@ __device__ __forceinline__ void gemm_tile_dec(const GemmParams& p, const TileInf
         issue(kt + STG - 1);
         const unsigned char* sa = smem + (kt % STG) * STAGE;
         const unsigned char* sb = sa + kDTileA;
+        // all twelve fragment reads of the k-step first, then the eight MFMAs: interleaved, each MFMA
+        // pair waited for its own reads (one LDS round trip each), which a wave alone on its SIMD (the
+        // one-wave tiles) cannot hide
+        bf16x8 fa[BK / 16], fb0[BK / 16], fb1[BK / 16];
 #pragma unroll
         for (int s = 0; s < BK / 16; ++s) {
             const int kc = 2 * s + (lane >> 5);
-            const bf16x8 a = frag(sa, lane & 31, kc);
-            const bf16x8 b0 = PK ? *reinterpret_cast<const bf16x8*>(sb + (8 * w + s) * 1024 + lane * 16)
-                                 : frag(sb, 64 * w + (lane & 31), kc);
-            const bf16x8 b1 = PK ? *reinterpret_cast<const bf16x8*>(sb + (8 * w + 4 + s) * 1024 + lane * 16)
-                                 : frag(sb, 64 * w + 32 + (lane & 31), kc);
-            acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b0, acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b1, acc1, 0, 0, 0);
+            fa[s] = frag(sa, lane & 31, kc);
+            fb0[s] = PK ? *reinterpret_cast<const bf16x8*>(sb + (8 * w + s) * 1024 + lane * 16)
+                        : frag(sb, 64 * w + (lane & 31), kc);
+            fb1[s] = PK ? *reinterpret_cast<const bf16x8*>(sb + (8 * w + 4 + s) * 1024 + lane * 16)
+                        : frag(sb, 64 * w + 32 + (lane & 31), kc);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int s = 0; s < BK / 16; ++s) {
+            acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s], fb0[s], acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s], fb1[s], acc1, 0, 0, 0);
         }
     }
     // drain the trailing (clamped) loads before the LDS is reused for staging
