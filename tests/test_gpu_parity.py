@@ -27,6 +27,9 @@ VARIANTS = {
     "swiglu_f32": RAGGED.with_(name="swiglu_f32", dtype=DT_F32, T=130),
     "renorm_softmax": RAGGED.with_(name="renorm_softmax", gating=GATE_SOFTMAX_RENORM, bias_var=0.0),
     "all_experts": RAGGED.with_(name="all_experts", K_r=16, Ks=1),
+    # 600 tokens: the shared down GEMM with the fused combine takes the 128 x 128 kernel, and K_r = 16
+    # routed rows per token take its epilogue without the LDS copy of the pair rows (that holds 12)
+    "all_experts_prefill": RAGGED.with_(name="all_experts_prefill", T=600, K_r=16, Ks=1),
     "no_shared": RAGGED.with_(name="no_shared", Ks=0, K_r=5),
     "group_limited": RAGGED.with_(name="group_limited", N_r=32, K_r=4, n_group=8, topk_group=2),
     "group_limited_softmax": RAGGED.with_(name="group_limited_softmax", N_r=32, K_r=4, n_group=4, topk_group=2,
