@@ -6,17 +6,23 @@
 //   SwiGLU: y = W2 (SiLU(Wg x) * (Wu x))      ReLU: y = V ReLU(W x + b)   (tomabc explainer)
 // computed as an "up" GEMM with the activation fused into its epilogue, then a "down" GEMM.
 //
-// bf16 path, all on v_mfma_f32_32x32x16_bf16 with persistent XCD-aware grids and operands in
-// double-buffered LDS:
-//  - 128 x 512 x 64 tiles, four waves of 128 x 128, operands register-staged with buffer loads
-//    (the prefill GEMMs: many rows per group);
-//  - 128 x 512 x 64 tiles, eight waves of 128 x 64, direct-to-LDS loads (the same GEMMs when an
-//    operand spans 2 GiB or more);
-//  - 128 x 128 x 64 tiles, four waves of 64 x 64, two workgroups per CU (decode-sized groups,
-//    the fused shared-down + combine, the router logits).
-// For SwiGLU the weight rows of a tile are gate rows and the matching up rows, so the epilogue
-// has both halves of every output element in the same lane.  fp32 path: plain VALU kernels (the
-// tiny fp32 layer only).
+// bf16 path, all on v_mfma_f32_32x32x16_bf16 with persistent XCD-aware grids:
+//  - k_gemm_bf16_w4p: routed weights in MFMA fragment order (launch_pack_b); 128 x 512 x 64 tiles,
+//    four waves of 128 x 128, each wave loading its weight fragments straight into registers and
+//    the activation tile going through a ring of direct-to-LDS loads (the prefill default); a
+//    128 x 256 instantiation at two workgroups per CU serves reductions of at most 512;
+//  - k_gemm_bf16_w4: the same 128 x 512 tile on [out, in] weights, both operands register-staged
+//    with buffer loads into double-buffered LDS (also the dense shared up projection);
+//  - k_gemm_bf16_wide8: 128 x 512 tiles, eight waves of 128 x 64, direct-to-LDS loads (operands
+//    spanning 2 GiB or more);
+//  - k_gemm_bf16: 128 x 128 x 64 tiles, four waves of 64 x 64, two workgroups per CU (the fused
+//    shared-down + combine, the prefill router logits, small problems);
+//  - k_gemm_bf16_dec: 32-row tiles with a deep direct-to-LDS load ring for decode-sized groups
+//    (four waves of 64 weight rows) and a one-wave variant for the few dense rows of a decode step.
+// Every kernel accumulates an output in one fp32 chain over ascending 16-deep k-chunks, so the
+// choice of kernel does not change a result bit.  For SwiGLU the weight rows of a tile are gate
+// rows and the matching up rows, so the epilogue has both halves of every output element in the
+// same lane.  fp32 path: plain VALU kernels (the tiny fp32 layer only).
 #include <stdlib.h>
 
 #include <type_traits>
