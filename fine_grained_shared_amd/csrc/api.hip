@@ -461,10 +461,12 @@ int moe_profile_enable(int32_t on) {
         if (g_prof.ev.empty()) {
             g_prof.ev.resize(2 * kProfPairs);
             g_prof.cls.resize(kProfPairs);
-            for (auto& e : g_prof.ev) {
-                const hipError_t r = hipEventCreate(&e);
+            for (size_t i = 0; i < g_prof.ev.size(); ++i) {
+                const hipError_t r = hipEventCreate(&g_prof.ev[i]);
                 if (r != hipSuccess) {
+                    for (size_t j = 0; j < i; ++j) (void)hipEventDestroy(g_prof.ev[j]);
                     g_prof.ev.clear();
+                    g_prof.cls.clear();
                     return hip_fail(r);
                 }
             }
