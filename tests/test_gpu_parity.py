@@ -122,6 +122,32 @@ def test_stage_dispatch_bit_exact(ragged, torch_cuda):
     assert torch.equal(x_perm, d["u"][row_token.long()])
 
 
+@pytest.mark.parametrize("T,N,K", [(5000, 300, 6), (20000, 1024, 8), (10000, 64, 2)])
+def test_dispatch_bit_exact_many_chunks(T, N, K, torch_cuda):
+    """Dispatch on skewed synthetic selections with many 256-token chunks: the scan runs one workgroup
+    per 64 experts (a partial last one at N = 300) with 16 chunk ranges per expert, some of them empty.
+    Offsets, rows and pair positions must equal the oracle's nested loops exactly."""
+    import fine_grained_shared_amd as moe
+    torch = torch_cuda
+    rng = np.random.default_rng(T + N + K)
+    skew = np.linspace(0.0, 3.0, N)[rng.permutation(N)]          # a few experts far more popular
+    keys = rng.random((T, N)) + skew[None, :]
+    idx_np = np.argsort(-keys, axis=1)[:, :K].astype(np.int32)    # K distinct experts per token
+    s = moe.make_shape(T, 64, N, K, 0, 64, synth.GATE_SOFTMAX, synth.ACT_SWIGLU, synth.DT_BF16)
+    ws = moe.workspace(s)
+    idx = torch.from_numpy(idx_np).cuda()
+    R = T * K
+    offsets = torch.full((N + 1,), -7, dtype=torch.int32, device="cuda")
+    row_token = torch.full((R,), -7, dtype=torch.int32, device="cuda")
+    pair_row = torch.full((R,), -7, dtype=torch.int32, device="cuda")
+    moe.moe_dispatch(s, idx, offsets, row_token, pair_row, None, None, ws)
+    torch.cuda.synchronize()
+    o_ref, rt_ref, pr_ref = oracle.dispatch(idx_np, N)
+    assert np.array_equal(offsets.cpu().numpy(), o_ref)
+    assert np.array_equal(row_token.cpu().numpy(), rt_ref)
+    assert np.array_equal(pair_row.cpu().numpy(), pr_ref)
+
+
 def test_stage_expert_ffn_both_gather_modes(ragged, torch_cuda):
     import fine_grained_shared_amd as moe
     torch = torch_cuda
