@@ -148,6 +148,46 @@ def test_dispatch_bit_exact_many_chunks(T, N, K, torch_cuda):
     assert np.array_equal(pair_row.cpu().numpy(), pr_ref)
 
 
+@pytest.mark.parametrize("T", [300, 1100])
+@pytest.mark.parametrize("gating", [GATE_SOFTMAX, GATE_SIGMOID_BIAS_NORM])
+def test_exact_ties_go_to_the_lower_index(T, gating, torch_cuda):
+    """Experts with identical centroids (and bias) tie exactly, on the GPU as in the oracle.  Pair
+    (5, 70) sits in different lanes of the selection wave (its index bits decide), pair (9, 73) in one
+    lane.  Tokens planted along one centroid of a pair must select [low, high] in that order with equal
+    gate weights.  T = 300 takes the decode-size logits kernel, T = 1100 the tiled GEMM."""
+    import fine_grained_shared_amd as moe
+    torch = torch_cuda
+    w = Workload("ties", "exact ties", T, 128, 128, 2, 0, 64, gating, ACT_SWIGLU, DT_BF16,
+                 bias_var=0.01 if gating == GATE_SIGMOID_BIAS_NORM else 0.0)
+    inp = synth.make_inputs(w, weights=False)
+    cen = inp["centroids"].copy()
+    u = inp["u"].copy()
+    bias = None if inp["bias"] is None else inp["bias"].copy()
+    plants = {}
+    for lo, hi in ((5, 70), (9, 73)):
+        cen[hi] = cen[lo]
+        if bias is not None:   # sigmoid saturates: the pair's lead comes from an equal, larger bias
+            bias[lo] = bias[hi] = 1.0
+        toks = np.arange(lo, T, 17)
+        # u_t = 16 e_lo (exact in bf16): the pair's logit 16 |e_lo|^2 dominates every other expert's
+        u[toks] = synth.f32_to_bf16_bits(16.0 * synth.bf16_bits_to_f32(cen[lo]))
+        plants[(lo, hi)] = toks
+    s = gpu_shape(w)
+    ws = moe.workspace(s)
+    idx = torch.empty((T, 2), dtype=torch.int32, device="cuda")
+    wts = torch.empty((T, 2), dtype=torch.float32, device="cuda")
+    moe.moe_route(s, to_dev(u), to_dev(cen), to_dev(bias), idx, wts, ws)
+    torch.cuda.synchronize()
+    got, g = idx.cpu().numpy(), wts.cpu().numpy()
+    for (lo, hi), toks in plants.items():
+        assert (got[toks] == [lo, hi]).all(), (lo, hi, got[toks][:4])
+        assert (g[toks, 0] == g[toks, 1]).all()
+    # the oracle agrees on the planted tokens (its keys tie exactly as well)
+    sel, _, _ = oracle.route(oracle.shape_of(w), u, cen, bias)
+    for (lo, hi), toks in plants.items():
+        assert (sel[toks] == [lo, hi]).all()
+
+
 def test_stage_expert_ffn_both_gather_modes(ragged, torch_cuda):
     import fine_grained_shared_amd as moe
     torch = torch_cuda
