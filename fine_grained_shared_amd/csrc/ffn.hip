@@ -156,6 +156,36 @@ __device__ __forceinline__ bool decode_tile(const GemmParams& p, int NT, int bm,
     return true;
 }
 
+// Grouped GEMMs keep the group table (an m-tile prefix and the row offsets, G + 1 entries each, G <=
+// 1024) in LDS: finding a tile's group is then a binary search over LDS instead of a chain of
+// dependent global loads at the start of every tile.
+constexpr int kGroupTabBytes = 2 * 1025 * 4;
+__device__ __forceinline__ void load_group_tab(const int32_t* tiles, const int32_t* offsets, int G, int32_t* gt) {
+    for (int i = threadIdx.x; i <= G; i += blockDim.x) {
+        gt[i] = tiles[i];
+        gt[G + 1 + i] = offsets[i];
+    }
+    __syncthreads();
+}
+// The tile L of the list whose m-tile prefix (tiles, of bm-row tiles) and offsets are in gt.
+__device__ __forceinline__ void decode_tile_tab(const int32_t* gt, int G, int NT, int bm, int L, TileInfo& ti) {
+    const int32_t* tiles = gt;
+    const int32_t* offs = gt + G + 1;
+    const int mt = L / NT;
+    int lo = 0, hi = G;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (tiles[mid] <= mt) lo = mid;
+        else hi = mid;
+    }
+    const int t0 = tiles[lo], nm = tiles[lo + 1] - t0;
+    int ml;
+    blocked_mn(L - t0 * NT, nm, NT, ml, ti.nt);
+    ti.g = lo;
+    ti.row0 = offs[lo] + ml * bm;
+    ti.rows = min(bm, offs[lo + 1] - ti.row0);
+}
+
 // ---------------------------------------------------------------- bf16 MFMA grouped GEMM
 // Persistent: the grid holds two workgroups per CU; the workgroups of one XCD walk a
 // contiguous range of the tile list (so concurrently running tiles of an XCD share weight
@@ -1112,7 +1142,8 @@ __host__ __device__ constexpr int p_smem(int mode, int nj) {
     return kPStages * kPStage > BM / 2 * (p_out_cols(mode, nj) + 16) * 4 ? kPStages * kPStage
                                                                           : BM / 2 * (p_out_cols(mode, nj) + 16) * 4;
 }
-static_assert(p_smem(GM_DOWN, 4) <= kWSmem && 2 * p_smem(GM_DOWN, 2) <= kWSmem, "A ring and staging must fit");
+static_assert(p_smem(GM_DOWN, 4) + kGroupTabBytes <= kWSmem && 2 * (p_smem(GM_DOWN, 2) + kGroupTabBytes) <= kWSmem,
+              "A ring, staging and group table must fit");
 
 // Epilogue of the packed kernel (grouped bf16 modes: SwiGLU, ReLU, down).  Each lane holds, for every
 // 32 x 32 accumulator block, rows 8 (q / 4) + 4 (lane / 32) + q % 4 of column lane % 32; the values are
@@ -1326,12 +1357,14 @@ __device__ __forceinline__ void gemm_tile_w4p(const GemmParams& p, const TileInf
 
 template <int MODE, bool A_FLAT, int NJ = 4>
 __global__ __launch_bounds__(256, 4 / NJ) void k_gemm_bf16_w4p(GemmParams p, int NT) {
-    __shared__ __attribute__((aligned(16))) unsigned char smem[p_smem(MODE, NJ)];
-    const int total = total_tiles(p, NT);
+    __shared__ __attribute__((aligned(16))) unsigned char smem[p_smem(MODE, NJ) + kGroupTabBytes];
+    int32_t* gt = reinterpret_cast<int32_t*>(smem + p_smem(MODE, NJ));
+    load_group_tab(p.tiles, p.offsets, p.G, gt);   // grouped only (checked at launch)
+    const int total = gt[p.G] * NT;
     const int xcd = blockIdx.x & 7, loc = blockIdx.x >> 3, per_xcd = gridDim.x >> 3;
     for (int L = window_tile(xcd, loc, per_xcd); L < total; L += (int)gridDim.x) {
         TileInfo ti;
-        decode_tile(p, NT, BM, L, ti);
+        decode_tile_tab(gt, p.G, NT, BM, L, ti);
         gemm_tile_w4p<MODE, A_FLAT, NJ>(p, ti, smem);
     }
 }
@@ -1504,9 +1537,12 @@ __global__ __launch_bounds__(64 * W) void k_gemm_bf16_dec(GemmParams p, int NT) 
     if (GROUPED != (p.offsets != nullptr)) return;  // launched with the matching instantiation only
     constexpr int SMEM = DSTAGES * (kDTileA + 64 * W * BK * 2);
     static_assert(DBM * DEPW * 4 <= SMEM, "decode epilogue staging must fit");
-    __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
+    static_assert(SMEM + kGroupTabBytes <= 160 * 1024, "LDS");
+    __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM + (GROUPED ? kGroupTabBytes : 0)];
+    int32_t* gt = reinterpret_cast<int32_t*>(smem + SMEM);
+    if (GROUPED) load_group_tab(p.tiles32, p.offsets, p.G, gt);
     const int nmd = (p.M_dense + DBM - 1) / DBM;     // dense: m-tiles per group
-    const int total = GROUPED ? p.tiles32[p.G] * NT : p.G * nmd * NT;
+    const int total = GROUPED ? gt[p.G] * NT : p.G * nmd * NT;
     const int xcd = blockIdx.x & 7, loc = blockIdx.x >> 3, per_xcd = gridDim.x >> 3;
     const int beg = (int)((long long)total * xcd / 8);
     const int end = (int)((long long)total * (xcd + 1) / 8);
@@ -1514,18 +1550,7 @@ __global__ __launch_bounds__(64 * W) void k_gemm_bf16_dec(GemmParams p, int NT) 
         TileInfo ti;
         int ml;
         if (GROUPED) {
-            const int mt = L / NT;
-            int lo = 0, hi = p.G;
-            while (hi - lo > 1) {
-                const int mid = (lo + hi) >> 1;
-                if (p.tiles32[mid] <= mt) lo = mid;
-                else hi = mid;
-            }
-            const int t0 = p.tiles32[lo], nm = p.tiles32[lo + 1] - t0;
-            blocked_mn(L - t0 * NT, nm, NT, ml, ti.nt);
-            ti.g = lo;
-            ti.row0 = p.offsets[lo] + ml * DBM;
-            ti.rows = min(DBM, p.offsets[lo + 1] - ti.row0);
+            decode_tile_tab(gt, p.G, NT, DBM, L, ti);
         } else {
             const int per = nmd * NT;
             ti.g = L / per;
