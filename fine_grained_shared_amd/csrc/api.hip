@@ -142,6 +142,11 @@ int do_route(const moe_shape* s, const void* u, const void* e, const float* bias
 int do_dispatch(const moe_shape* s, const int32_t* idx, int32_t* offsets, int32_t* row_token, int32_t* pair_row,
                 int32_t* chunks, hipStream_t st) {
     const int nchunk = (s->T + moe::kChunk - 1) / moe::kChunk;
+    if (nchunk == 1 && s->K_r > 0) {   // a decode step: one launch
+        MOE_TRY(MOE_PROF_DISPATCH, st,
+                moe::launch_dispatch1(idx, s->T, s->K_r, s->N_r, offsets, row_token, pair_row, st));
+        return MOE_OK;
+    }
     MOE_TRY(MOE_PROF_DISPATCH, st, moe::launch_count(idx, s->T, s->K_r, s->N_r, chunks, st));
     int32_t* bases = chunks + (size_t)nchunk * s->N_r;
     MOE_TRY(MOE_PROF_DISPATCH, st,

@@ -160,6 +160,70 @@ __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ idx
     }
 }
 
+// The whole dispatch of one chunk (T <= kChunk tokens, a decode step) in one workgroup: the histogram,
+// the exclusive prefix over the experts (offsets) and the stable scatter, all through LDS, in place of
+// the three launches above.  Positions are the same: offsets[e] + tokens before t in the chunk that
+// chose e.
+__global__ __launch_bounds__(256) void k_dispatch1(const int32_t* __restrict__ idx, int T, int K, int N,
+                                                   int32_t* __restrict__ offsets, int32_t* __restrict__ row_token,
+                                                   int32_t* __restrict__ pair_row) {
+    constexpr int W = kChunk / 32;
+    extern __shared__ uint32_t sh1[];
+    int32_t* base = reinterpret_cast<int32_t*>(sh1);   // [N]: counts, then segment starts
+    uint32_t* bits = sh1 + N;                          // [N][W]: tokens of the chunk per expert
+    __shared__ int32_t wsum[4];
+    const int tid = threadIdx.x;
+    for (int q = tid; q < N * (W + 1); q += 256) sh1[q] = 0u;
+    __syncthreads();
+    if (tid < T) {
+        for (int k = 0; k < K; ++k) {
+            const int e = idx[(size_t)tid * K + k];
+            if ((unsigned)e < (unsigned)N) {
+                atomicAdd(&base[e], 1);
+                atomicOr(&bits[e * W + (tid >> 5)], 1u << (tid & 31));
+            }
+        }
+    }
+    __syncthreads();
+    // exclusive prefix over the experts: thread tid sums experts [per tid, per (tid + 1)), then a block scan
+    const int per = (N + 255) / 256;
+    const int e0 = min(tid * per, N), e1 = min(e0 + per, N);
+    int run = 0;
+    for (int e = e0; e < e1; ++e) run += base[e];
+    const int lane = tid & 63, w = tid >> 6;
+    int incl = run;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int v = __shfl_up(incl, o);
+        if (lane >= o) incl += v;
+    }
+    if (lane == 63) wsum[w] = incl;
+    __syncthreads();
+    int acc = 0;
+    for (int q = 0; q < w; ++q) acc += wsum[q];
+    int start = acc + incl - run;
+    if (tid == 255) offsets[N] = acc + incl;
+    __syncthreads();   // every count read before the starts overwrite them
+    for (int e = e0; e < e1; ++e) {
+        const int c = base[e];
+        base[e] = start;
+        offsets[e] = start;
+        start += c;
+    }
+    __syncthreads();
+    if (tid < T) {
+        for (int k = 0; k < K; ++k) {
+            const int e = idx[(size_t)tid * K + k];
+            if ((unsigned)e >= (unsigned)N) continue;
+            int rank = __popc(bits[e * W + (tid >> 5)] & ((1u << (tid & 31)) - 1u));
+            for (int q = 0; q < (tid >> 5); ++q) rank += __popc(bits[e * W + q]);
+            const int pos = base[e] + rank;
+            row_token[pos] = tid;
+            pair_row[(size_t)tid * K + k] = pos;
+        }
+    }
+}
+
 template <typename E>
 __global__ __launch_bounds__(256) void k_gather(const E* __restrict__ u, const int32_t* __restrict__ row_token,
                                                 int R, int H, E* __restrict__ x_perm) {
@@ -193,6 +257,13 @@ hipError_t launch_scatter(const int32_t* idx, int T, int K, int N, const int32_t
     if (nchunk == 0 || K == 0) return hipSuccess;
     hipLaunchKernelGGL(k_scatter, dim3(nchunk), dim3(256), (size_t)N * (kChunk / 32) * sizeof(uint32_t), s, idx,
                        T, K, N, chunk_base, row_token, pair_row);
+    return hipGetLastError();
+}
+
+hipError_t launch_dispatch1(const int32_t* idx, int T, int K, int N, int32_t* offsets, int32_t* row_token,
+                            int32_t* pair_row, hipStream_t s) {
+    hipLaunchKernelGGL(k_dispatch1, dim3(1), dim3(256), (size_t)N * (kChunk / 32 + 1) * sizeof(uint32_t), s, idx, T,
+                       K, N, offsets, row_token, pair_row);
     return hipGetLastError();
 }
 

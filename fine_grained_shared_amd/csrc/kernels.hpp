@@ -34,6 +34,9 @@ hipError_t launch_scan(const int32_t* chunk_counts, int32_t* chunk_base, int nch
                        hipStream_t s);
 hipError_t launch_scatter(const int32_t* idx, int T, int K, int N, const int32_t* chunk_base,
                           int32_t* row_token, int32_t* pair_row, hipStream_t s);
+// all of the above for one chunk (1 <= T <= kChunk, K >= 1) in one launch
+hipError_t launch_dispatch1(const int32_t* idx, int T, int K, int N, int32_t* offsets, int32_t* row_token,
+                            int32_t* pair_row, hipStream_t s);
 hipError_t launch_gather(int dtype, const void* u, const int32_t* row_token, int R, int H, void* x_perm,
                          hipStream_t s);
 

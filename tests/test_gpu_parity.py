@@ -122,11 +122,13 @@ def test_stage_dispatch_bit_exact(ragged, torch_cuda):
     assert torch.equal(x_perm, d["u"][row_token.long()])
 
 
-@pytest.mark.parametrize("T,N,K", [(5000, 300, 6), (20000, 1024, 8), (10000, 64, 2)])
+@pytest.mark.parametrize("T,N,K", [(5000, 300, 6), (20000, 1024, 8), (10000, 64, 2),
+                                   (200, 300, 6), (256, 1024, 8), (37, 16, 16), (1, 64, 2)])
 def test_dispatch_bit_exact_many_chunks(T, N, K, torch_cuda):
-    """Dispatch on skewed synthetic selections with many 256-token chunks: the scan runs one workgroup
-    per 64 experts (a partial last one at N = 300) with 16 chunk ranges per expert, some of them empty.
-    Offsets, rows and pair positions must equal the oracle's nested loops exactly."""
+    """Dispatch on skewed synthetic selections.  Many 256-token chunks: the scan runs one workgroup per
+    64 experts (a partial last one at N = 300) with 16 chunk ranges per expert, some of them empty.
+    One chunk (T <= 256, a decode step): the single-launch path.  Offsets, rows and pair positions must
+    equal the oracle's nested loops exactly."""
     import fine_grained_shared_amd as moe
     torch = torch_cuda
     rng = np.random.default_rng(T + N + K)
