@@ -1443,8 +1443,8 @@ __device__ __forceinline__ void gemm_tile_dec(const GemmParams& p, const TileInf
         bg[i] = Bg + (size_t)wr * p.ldb + ((i & 1) ? kcg1 : kcg0);
     }
     const int nk = p.K / BK;
-    auto issue = [&](int kt) {   // k-tile min(kt, nk - 1) into its stage
-        const int k = (kt < nk ? kt : nk - 1) * BK;
+    auto issue = [&](int kt) {   // k-tile kt (< nk) into its stage
+        const int k = kt * BK;
         const int seg = k / p.Kseg;
         // packed: a 64-wide k-tile is four consecutive 1 KB fragments (2048 elements) per row block
         const long long bo = PK ? (long long)k * 32 : (long long)seg * p.sB_seg + (k - seg * p.Kseg);
@@ -1466,16 +1466,21 @@ __device__ __forceinline__ void gemm_tile_dec(const GemmParams& p, const TileInf
     }
     __syncthreads();   // the previous tile's epilogue may still read the LDS staging area
 #pragma unroll
-    for (int u = 0; u < STG - 1; ++u) issue(u);
+    for (int u = 0; u < STG - 1; ++u)
+        if (u < nk) issue(u);
     for (int kt = 0; kt < nk; ++kt) {
         // this wave's loads of k-tile kt have landed once at most the STG - 2 newer k-tiles (NA + 8
         // loads each) are outstanding; the barrier then covers every wave's loads and every wave's
         // reads of the stage k-step kt-1 used, which the next issue overwrites
         asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_waitcnt(waitcnt_imm((STG - 2) * (NA + 8), 0));
+        // k-tiles past the end are not issued, so near the end fewer newer loads can be outstanding
+        static_assert(STG == 4, "the wait counts assume four stages");
+        if (kt + 2 < nk) __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * (NA + 8), 0));
+        else if (kt + 1 < nk) __builtin_amdgcn_s_waitcnt(waitcnt_imm(NA + 8, 0));
+        else __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        issue(kt + STG - 1);
+        if (kt + STG - 1 < nk) issue(kt + STG - 1);
         const unsigned char* sa = smem + (kt % STG) * STAGE;
         const unsigned char* sb = sa + kDTileA;
         // all twelve fragment reads of the k-step first, then the eight MFMAs: interleaved, each MFMA
