@@ -4,9 +4,9 @@ One step = one call of moe_layer_forward (router, dispatch, routed + shared expe
 combine + residual) over the V3-style workload: T=16384 tokens, H=7168, 1 shared + 256 routed
 SwiGLU experts of width 2048, top-8, sigmoid + selection bias, bf16 with fp32 accumulation.
 Inputs are seeded synthetic tensors of that shape (no trained weights), resident in HBM before
-timing starts.  The routed expert weights are stored in fragment order by default (moe_pack_weights,
-done once when the weights are loaded, outside the timed steps; --weights unpacked keeps the
-[out, in] layout, with bit-identical results).  The decode regime (the first 128 tokens of the
+timing starts.  The routed expert banks and the shared experts' gate/up bank are stored in fragment
+order by default (moe_pack_weights, done once when the weights are loaded, outside the timed steps;
+--weights unpacked keeps the [out, in] layout, with bit-identical results).  The decode regime (the first 128 tokens of the
 same inputs) is timed as well.
 
 Prints one JSON line.  Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
@@ -331,10 +331,11 @@ def main():
     if args.weights == "packed":
         # a storage layout of the same weights, made once when they are loaded (not part of a step);
         # the [out, in] banks are kept to time the same step on them as well
-        unpacked = None if args.no_unpacked else {k: d[k] for k in ("w1", "w2")}
-        for k in ("w1", "w2"):
+        packed_keys = ("w1", "w2") + (("w1_sh",) if w.Ks > 0 else ())
+        unpacked = None if args.no_unpacked else {k: d[k] for k in packed_keys}
+        for k in packed_keys:
             d[k] = moe.pack_weights(d[k])
-        flags = moe.MOE_FLAG_PACKED_WEIGHTS
+        flags = moe.MOE_FLAG_PACKED_WEIGHTS | (moe.MOE_FLAG_PACKED_SHARED_UP if w.Ks > 0 else 0)
     torch.cuda.synchronize()
     print("[bench] inputs generated in %.1f s and uploaded (%s routed banks)" % (gen_s, args.weights),
           file=sys.stderr, flush=True)
@@ -382,7 +383,9 @@ def main():
         "config": {"workload": w.desc, "T": w.T, "H": w.H, "N_r": w.N_r, "K_r": w.K_r, "Ks": w.Ks, "I": w.I,
                    "gating": "sigmoid+selection bias, normalised over selected",
                    "act": "SwiGLU", "parallelism": "single GPU",
-                   "routed_weights": "fragment order (packed once at load)" if flags else "[out, in]"},
+                   "routed_weights": "fragment order (packed once at load)" if flags else "[out, in]",
+                   "shared_up_weights": ("fragment order (packed once at load)"
+                                         if flags & moe.MOE_FLAG_PACKED_SHARED_UP else "[out, in]")},
         "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
         "pct_bf16_peak": round(100 * flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
         "roofline": {"kernel": "routed expert gate/up grouped GEMM + SwiGLU (%s)" % dominant_kernel(flags),
@@ -399,11 +402,11 @@ def main():
     if unpacked is not None:
         def ustep():
             moe.moe_layer_forward(shape, d["u"], d["centroids"], d["bias"], unpacked["w1"], d["b1"], unpacked["w2"],
-                                  d["w1_sh"], d["b1_sh"], d["w2_sh"], 0, out, idx, wts, ws)
+                                  unpacked.get("w1_sh", d["w1_sh"]), d["b1_sh"], d["w2_sh"], 0, out, idx, wts, ws)
 
         ums = _time_steps(ustep, max(5, args.steps // 2), args.warmup)
         result["unpacked_weights"] = {"ms_per_step": round(ums, 4), "value": round(w.T / (ums * 1e-3), 1),
-                                      "note": "the same step on the [out, in] routed banks (bit-identical output)"}
+                                      "note": "the same step on the [out, in] banks (bit-identical output)"}
         print("[bench] prefill, [out, in] routed banks: %.3f ms/step" % ums, file=sys.stderr, flush=True)
         del unpacked
         torch.cuda.empty_cache()

@@ -24,6 +24,7 @@ MOE_ACT_RELU_BIAS, MOE_ACT_SWIGLU = 0, 1
 MOE_F32, MOE_BF16 = 0, 1
 MOE_FLAG_NO_RESIDUAL = 1
 MOE_FLAG_PACKED_WEIGHTS = 2
+MOE_FLAG_PACKED_SHARED_UP = 4
 (MOE_PROF_ROUTER, MOE_PROF_DISPATCH, MOE_PROF_FFN_UP, MOE_PROF_FFN_DOWN, MOE_PROF_SHARED_UP,
  MOE_PROF_SHARED_DOWN, MOE_PROF_COMBINE, MOE_PROF_OTHER) = range(8)
 PROF_NAMES = ["router", "dispatch", "ffn_up", "ffn_down", "shared_up", "shared_down", "combine", "other"]

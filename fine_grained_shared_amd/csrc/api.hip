@@ -221,7 +221,7 @@ struct Combine {
 };
 
 int do_shared_ffn(const moe_shape* s, const void* x, const void* w1, const float* b1, const void* w2, void* y,
-                  void* act, hipStream_t st, const Combine* comb = nullptr) {
+                  void* act, hipStream_t st, const Combine* comb = nullptr, bool packed_up = false) {
     if (s->T == 0 || s->Ks == 0) return MOE_OK;
     const int n1 = s->act == MOE_ACT_SWIGLU ? 2 * s->I : s->I;
     moe::GemmParams up{};
@@ -243,6 +243,7 @@ int do_shared_ffn(const moe_shape* s, const void* x, const void* w1, const float
     up.sC_group = s->I;
     up.bias = b1;
     up.sbias_group = s->I;
+    up.packed = packed_up;
     const int up_mode = s->act == MOE_ACT_SWIGLU ? moe::GM_UP_SWIGLU : moe::GM_UP_RELU;
     MOE_TRY(MOE_PROF_SHARED_UP, st, moe::launch_gemm(s->dtype, up_mode, up, st));
     // down: one GEMM whose reduction runs over the Ks intermediates side by side
@@ -393,9 +394,11 @@ int moe_layer_forward(const moe_shape* s, const void* u, const void* centroids, 
                       void* stream) {
     int rc = check_shape(s);
     if (rc != MOE_OK) return rc;
-    if (flags & ~(MOE_FLAG_NO_RESIDUAL | MOE_FLAG_PACKED_WEIGHTS)) return MOE_ERR_INVALID_ARG;
+    if (flags & ~(MOE_FLAG_NO_RESIDUAL | MOE_FLAG_PACKED_WEIGHTS | MOE_FLAG_PACKED_SHARED_UP))
+        return MOE_ERR_INVALID_ARG;
     const bool packed = (flags & MOE_FLAG_PACKED_WEIGHTS) != 0;
-    if (packed && (rc = check_packed(s)) != MOE_OK) return rc;
+    const bool packed_sh = (flags & MOE_FLAG_PACKED_SHARED_UP) != 0;
+    if ((packed || packed_sh) && (rc = check_packed(s)) != MOE_OK) return rc;
     if (bias && s->gating != MOE_GATE_SIGMOID_BIAS_NORM) return MOE_ERR_INVALID_ARG;
     if ((b1 || b1_sh) && s->act != MOE_ACT_RELU_BIAS) return MOE_ERR_INVALID_ARG;
     if (s->T == 0) return MOE_OK;
@@ -426,10 +429,12 @@ int moe_layer_forward(const moe_shape* s, const void* u, const void* centroids, 
         // combine fused into the shared experts' down GEMM: the shared output never leaves the
         // fp32 accumulators, and the layer output is written once
         const Combine comb{resid, y_perm, pair_row, wts};
-        return do_shared_ffn(s, u, w1_sh, b1_sh, w2_sh, out, at<void>(ws, L.act_sh), st, &comb);
+        return do_shared_ffn(s, u, w1_sh, b1_sh, w2_sh, out, at<void>(ws, L.act_sh), st, &comb, packed_sh);
     }
     if (s->Ks > 0) {
-        if ((rc = do_shared_ffn(s, u, w1_sh, b1_sh, w2_sh, y_sh, at<void>(ws, L.act_sh), st)) != MOE_OK) return rc;
+        if ((rc = do_shared_ffn(s, u, w1_sh, b1_sh, w2_sh, y_sh, at<void>(ws, L.act_sh), st, nullptr, packed_sh)) !=
+            MOE_OK)
+            return rc;
     }
     MOE_TRY(MOE_PROF_COMBINE, st,
             moe::launch_combine(s->dtype, resid, s->Ks > 0 ? y_sh : nullptr, y_perm, pair_row, wts, out, s->T, s->H,

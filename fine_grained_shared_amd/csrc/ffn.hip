@@ -1196,6 +1196,7 @@ __device__ __forceinline__ void w4p_epilogue(const GemmParams& p, const TileInfo
     __syncthreads();
     constexpr int G = OUTW / 8;   // 8-column groups per row pair
     uint16_t* C = (uint16_t*)p.C;
+    const long long coff = p.offsets ? 0 : (long long)ti.g * p.sC_group;   // dense groups side by side
     for (int it = tid; it < BM / 2 * G; it += 256) {
         const int rp = it / G, cg = it - rp * G;
         const int r0 = 2 * rp;
@@ -1213,8 +1214,9 @@ __device__ __forceinline__ void w4p_epilogue(const GemmParams& p, const TileInfo
         hi.z = __builtin_amdgcn_perm(y.y, y.x, 0x07060302u);
         hi.w = __builtin_amdgcn_perm(y.w, y.z, 0x07060302u);
         const long long row = ti.row0 + r0;
-        *reinterpret_cast<uint4*>(C + row * p.ldc + col0) = lo;
-        if (r0 + 1 < ti.rows) *reinterpret_cast<uint4*>(C + (row + 1) * p.ldc + col0) = hi;
+        uint16_t* c = C + row * p.ldc + coff + col0;
+        *reinterpret_cast<uint4*>(c) = lo;
+        if (r0 + 1 < ti.rows) *reinterpret_cast<uint4*>(c + p.ldc) = hi;
     }
 }
 
@@ -1359,12 +1361,13 @@ template <int MODE, bool A_FLAT, int NJ = 4>
 __global__ __launch_bounds__(256, 4 / NJ) void k_gemm_bf16_w4p(GemmParams p, int NT) {
     __shared__ __attribute__((aligned(16))) unsigned char smem[p_smem(MODE, NJ) + kGroupTabBytes];
     int32_t* gt = reinterpret_cast<int32_t*>(smem + p_smem(MODE, NJ));
-    load_group_tab(p.tiles, p.offsets, p.G, gt);   // grouped only (checked at launch)
-    const int total = gt[p.G] * NT;
+    if (p.offsets) load_group_tab(p.tiles, p.offsets, p.G, gt);
+    const int total = p.offsets ? gt[p.G] * NT : total_tiles(p, NT);
     const int xcd = blockIdx.x & 7, loc = blockIdx.x >> 3, per_xcd = gridDim.x >> 3;
     for (int L = window_tile(xcd, loc, per_xcd); L < total; L += (int)gridDim.x) {
         TileInfo ti;
-        decode_tile_tab(gt, p.G, NT, BM, L, ti);
+        if (p.offsets) decode_tile_tab(gt, p.G, NT, BM, L, ti);
+        else decode_tile(p, NT, BM, L, ti);   // dense: every group covers rows [0, M_dense)
         gemm_tile_w4p<MODE, A_FLAT, NJ>(p, ti, smem);
     }
 }
@@ -1652,11 +1655,34 @@ hipError_t launch_gemm(int dtype, int mode, const GemmParams& p_in, hipStream_t 
     if (mode == GM_DOWN_COMBINE && p.offsets) return hipErrorInvalidValue;  // dense (shared) groups only
     const long long cus = device_cus();
     if (p.packed) {
-        // fragment-order weights: routed (grouped) up/down GEMMs, one K segment, 32-bit offsets
-        if (!p.offsets || !p.tiles32 || p.Kseg != p.K || p.b_bytes == 0 || p.N % 32 ||
-            !(mode == GM_UP_SWIGLU || mode == GM_UP_RELU || mode == GM_DOWN))
+        // fragment-order weights: grouped (routed) or dense (shared, all groups on the same rows) up/down
+        // GEMMs, one K segment, 32-bit offsets
+        if ((p.offsets && !p.tiles32) || (!p.offsets && p.sA_group != 0) || p.Kseg != p.K || p.b_bytes == 0 ||
+            p.N % 32 || !(mode == GM_UP_SWIGLU || mode == GM_UP_RELU || mode == GM_DOWN))
             return hipErrorInvalidValue;
-        const long long rpg = p.max_rows / p.G;
+        if (!p.offsets && p.M_dense < 512) {
+            // a few dense rows (the shared experts of a decode step): 32-row tiles
+            const int NTd = mode == GM_UP_SWIGLU ? (p.N + DBN / 2 - 1) / (DBN / 2) : (p.N + DBN - 1) / DBN;
+            const long long mtd = (long long)p.G * ((p.M_dense + DBM - 1) / DBM);
+            if (mtd * NTd < cus) {   // one-wave workgroups of 64 weight rows, three per CU
+                const int NT1 = mode == GM_UP_SWIGLU ? (p.N + 31) / 32 : (p.N + 63) / 64;
+                long long nb1 = mtd * NT1;
+                nb1 = nb1 < 3 * cus ? nb1 : 3 * cus;
+                const dim3 grid1((unsigned)((nb1 + 7) / 8 * 8));
+                if (mode == GM_UP_SWIGLU) hipLaunchKernelGGL((k_gemm_bf16_dec<GM_UP_SWIGLU, false, true, 1>), grid1, dim3(64), 0, s, p, NT1);
+                else if (mode == GM_UP_RELU) hipLaunchKernelGGL((k_gemm_bf16_dec<GM_UP_RELU, false, true, 1>), grid1, dim3(64), 0, s, p, NT1);
+                else hipLaunchKernelGGL((k_gemm_bf16_dec<GM_DOWN, false, true, 1>), grid1, dim3(64), 0, s, p, NT1);
+                return hipGetLastError();
+            }
+            long long nb = (mtd * NTd + 7) / 8 * 8;
+            nb = nb < cus ? nb : cus;
+            const dim3 grid((unsigned)((nb + 7) / 8 * 8));
+            if (mode == GM_UP_SWIGLU) hipLaunchKernelGGL((k_gemm_bf16_dec<GM_UP_SWIGLU, false, true>), grid, dim3(256), 0, s, p, NTd);
+            else if (mode == GM_UP_RELU) hipLaunchKernelGGL((k_gemm_bf16_dec<GM_UP_RELU, false, true>), grid, dim3(256), 0, s, p, NTd);
+            else hipLaunchKernelGGL((k_gemm_bf16_dec<GM_DOWN, false, true>), grid, dim3(256), 0, s, p, NTd);
+            return hipGetLastError();
+        }
+        const long long rpg = p.offsets ? p.max_rows / p.G : p.M_dense;
         if (rpg < 64) {   // decode-sized groups: 32-row tiles, deep direct-to-LDS pipeline
             const int NTd = mode == GM_UP_SWIGLU ? (p.N + DBN / 2 - 1) / (DBN / 2) : (p.N + DBN - 1) / DBN;
             const long long mtd = (p.max_rows + DBM - 1) / DBM + p.G;
@@ -1673,7 +1699,8 @@ hipError_t launch_gemm(int dtype, int mode, const GemmParams& p_in, hipStream_t 
         // doubled activation traffic than they gain
         const int nj = p.K <= 512 ? 2 : 4;
         const int NTp = (p.N + p_out_cols(mode, nj) - 1) / p_out_cols(mode, nj);
-        const long long mtp = (p.max_rows + BM - 1) / BM + p.G;
+        const long long mtp = p.offsets ? (p.max_rows + BM - 1) / BM + p.G
+                                        : (long long)p.G * ((p.M_dense + BM - 1) / BM);
         long long nb = (mtp * NTp + 7) / 8 * 8;
         const long long slots = nj == 2 ? 2 * cus : cus;
         nb = nb < slots ? nb : slots;

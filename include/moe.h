@@ -74,8 +74,9 @@ enum { MOE_F32 = 0, MOE_BF16 = 1 };
 
 /* moe_layer_forward flags */
 enum {
-    MOE_FLAG_NO_RESIDUAL = 1,   /* drop the + u_t term: returns the MoE part only */
-    MOE_FLAG_PACKED_WEIGHTS = 2 /* routed banks w1, w2 are in fragment order (moe_pack_weights) */
+    MOE_FLAG_NO_RESIDUAL = 1,      /* drop the + u_t term: returns the MoE part only */
+    MOE_FLAG_PACKED_WEIGHTS = 2,   /* routed banks w1, w2 are in fragment order (moe_pack_weights) */
+    MOE_FLAG_PACKED_SHARED_UP = 4  /* the shared up bank w1_sh is in fragment order (moe_pack_weights) */
 };
 
 typedef struct moe_shape {
@@ -187,8 +188,10 @@ int moe_combine(const moe_shape* shape, const void* residual, const void* y_shar
  * The whole layer: route -> dispatch -> routed FFNs + shared FFNs -> combine + residual.
  *   u [T, H]; centroids [N_r, H]; bias [N_r] | NULL; routed banks (G = N_r); shared banks
  *   (G = Ks, NULL when Ks == 0); flags: MOE_FLAG_*; out [T, H] dtype.
- *   MOE_FLAG_PACKED_WEIGHTS: w1 and w2 (routed) are packed by moe_pack_weights (bf16 only); the
- *   shared banks stay [out, in]; the output is bit-identical to the unpacked call.
+ *   MOE_FLAG_PACKED_WEIGHTS: w1 and w2 (routed) are packed by moe_pack_weights (bf16 only).
+ *   MOE_FLAG_PACKED_SHARED_UP: w1_sh (the shared experts' gate/up bank, [Ks, n1, H]) is packed by
+ *   moe_pack_weights (bf16 only); w2_sh stays [out, in] (its GEMM also performs the combine).
+ *   Either way the output is bit-identical to the unpacked call.
  *   topk_idx_out [T, K_r], topk_w_out [T, K_r]: optional copies of the routing (NULL = none).
  */
 int moe_layer_forward(const moe_shape* shape, const void* u, const void* centroids, const float* bias,

@@ -78,7 +78,7 @@ def test_calls_rejected_before_any_launch():
 
 
 def test_packed_weight_calls_rejected_before_any_launch():
-    """moe_pack_weights / moe_expert_ffn_packed / MOE_FLAG_PACKED_WEIGHTS argument checks (host only:
+    """moe_pack_weights / moe_expert_ffn_packed / MOE_FLAG_PACKED_* argument checks (host only:
     the pointers are never dereferenced because every case is rejected before a launch)."""
     import ctypes
     lib = moe.load()
@@ -95,9 +95,12 @@ def test_packed_weight_calls_rejected_before_any_launch():
     s32 = moe.make_shape(16, 128, 16, 4, 1, 64, 0, 1, moe.MOE_F32)
     assert lib.moe_expert_ffn_packed(ctypes.byref(s32), A, None, A, A, None, A, A, A, 1 << 30, None) == \
         moe.MOE_ERR_INVALID_ARG
-    assert lib.moe_layer_forward(ctypes.byref(s32), None, None, None, None, None, None, None, None, None,
-                                 moe.MOE_FLAG_PACKED_WEIGHTS, None, None, None, None, 0, None) == \
-        moe.MOE_ERR_INVALID_ARG
+    for flag in (moe.MOE_FLAG_PACKED_WEIGHTS, moe.MOE_FLAG_PACKED_SHARED_UP):
+        assert lib.moe_layer_forward(ctypes.byref(s32), None, None, None, None, None, None, None, None, None,
+                                     flag, None, None, None, None, 0, None) == moe.MOE_ERR_INVALID_ARG
+    s16 = moe.make_shape(16, 128, 16, 4, 1, 64, 0, 1, moe.MOE_BF16)
+    assert lib.moe_layer_forward(ctypes.byref(s16), None, None, None, None, None, None, None, None, None,
+                                 8, None, None, None, None, 0, None) == moe.MOE_ERR_INVALID_ARG   # unknown flag
     # bf16 with too large an expert matrix for 32-bit offsets
     sbig = moe.make_shape(16, 65536, 16, 4, 0, 16384, 0, 1, moe.MOE_BF16)
     assert lib.moe_layer_forward(ctypes.byref(sbig), None, None, None, None, None, None, None, None, None,

@@ -4,8 +4,8 @@ The packing kernel is checked against the layout written out on the host.  The p
 packed expert FFN are checked against the unpacked ones bit for bit: every GEMM kernel accumulates an
 output in one fixed order, so the storage order of the weights cannot change a result.  One packed
 layer is also compared with the oracle.  The shapes cover the packed kernels (the 128 x 512 tile, the
-128 x 256 tile of reductions up to 512 and the 32-row decode tile), odd k-step counts, ragged column
-tiles and empty expert groups.
+128 x 256 tile of reductions up to 512 and the 32-row decode tile, grouped for the routed experts and
+dense for the shared up bank), odd k-step counts, ragged column tiles and empty expert groups.
 """
 import gc
 
@@ -53,15 +53,21 @@ def torch_cuda():
     return torch
 
 
-def packed_case(case):
-    """The same case with the routed banks packed on the GPU (and the flag set for its forward)."""
+def packed_case(case, routed=True, shared=True):
+    """The same case with the routed banks and / or the shared up bank packed on the GPU (and the flags
+    set for its forward)."""
     import fine_grained_shared_amd as moe
     c = Case.__new__(Case)
     c.w, c.inp = case.w, case.inp
     c.dev = dict(case.dev)
-    c.dev["w1"] = moe.pack_weights(case.dev["w1"])
-    c.dev["w2"] = moe.pack_weights(case.dev["w2"])
-    c.extra_flags = moe.MOE_FLAG_PACKED_WEIGHTS
+    c.extra_flags = 0
+    if routed:
+        c.dev["w1"] = moe.pack_weights(case.dev["w1"])
+        c.dev["w2"] = moe.pack_weights(case.dev["w2"])
+        c.extra_flags |= moe.MOE_FLAG_PACKED_WEIGHTS
+    if shared and case.w.Ks > 0:
+        c.dev["w1_sh"] = moe.pack_weights(case.dev["w1_sh"])
+        c.extra_flags |= moe.MOE_FLAG_PACKED_SHARED_UP
     return c
 
 
@@ -96,6 +102,14 @@ def test_pack_layout(torch_cuda):
 def test_packed_layer_bit_identical(torch_cuda, name):
     case = Case(VARIANTS[name])
     assert_same_layer(case, packed_case(case), name)
+
+
+@pytest.mark.parametrize("name", ["ragged", "ragged_decode", "relu"])
+def test_packed_shared_up_only_bit_identical(torch_cuda, name):
+    """Only the shared up bank packed: the dense packed GEMM (two shared experts side by side, 600 rows
+    on the 128-row tiles, 40 rows on the 32-row decode tiles) next to [out, in] routed banks."""
+    case = Case(VARIANTS[name])
+    assert_same_layer(case, packed_case(case, routed=False), name + "_shared_only")
 
 
 def test_packed_layer_against_oracle(torch_cuda):
