@@ -28,7 +28,7 @@ import numpy as np
 
 METRIC = "MoE-layer tokens/s and TFLOP/s (% bf16 MFMA peak) at V3-style shape; decode HBM GB/s"
 # routed gate/up grouped GEMM + SwiGLU: [out, in] banks, and banks in fragment order (moe_pack_weights)
-DOMINANT_KERNELS = ("k_gemm_bf16_w4<0, true>", "k_gemm_bf16_w4p<0, false, 4>")
+DOMINANT_KERNELS = ("k_gemm_bf16_w4<0, true>", "k_gemm_bf16_w4p<0, false, 4, true>")
 
 
 def dominant_kernel(flags):

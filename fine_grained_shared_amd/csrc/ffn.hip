@@ -1357,17 +1357,20 @@ __device__ __forceinline__ void gemm_tile_w4p(const GemmParams& p, const TileInf
     w4p_epilogue<MODE, NJ>(p, ti, acc, smem);
 }
 
-template <int MODE, bool A_FLAT, int NJ = 4>
+// GROUPED: routed segments (group table in LDS); otherwise dense groups, every group over the rows
+// [0, M_dense) (the shared experts).  Separate instantiations, so a profile tells them apart.
+template <int MODE, bool A_FLAT, int NJ = 4, bool GROUPED = true>
 __global__ __launch_bounds__(256, 4 / NJ) void k_gemm_bf16_w4p(GemmParams p, int NT) {
+    if (GROUPED != (p.offsets != nullptr)) return;  // launched with the matching instantiation only
     __shared__ __attribute__((aligned(16))) unsigned char smem[p_smem(MODE, NJ) + kGroupTabBytes];
     int32_t* gt = reinterpret_cast<int32_t*>(smem + p_smem(MODE, NJ));
-    if (p.offsets) load_group_tab(p.tiles, p.offsets, p.G, gt);
-    const int total = p.offsets ? gt[p.G] * NT : total_tiles(p, NT);
+    if (GROUPED) load_group_tab(p.tiles, p.offsets, p.G, gt);
+    const int total = GROUPED ? gt[p.G] * NT : total_tiles(p, NT);
     const int xcd = blockIdx.x & 7, loc = blockIdx.x >> 3, per_xcd = gridDim.x >> 3;
     for (int L = window_tile(xcd, loc, per_xcd); L < total; L += (int)gridDim.x) {
         TileInfo ti;
-        if (p.offsets) decode_tile_tab(gt, p.G, NT, BM, L, ti);
-        else decode_tile(p, NT, BM, L, ti);   // dense: every group covers rows [0, M_dense)
+        if (GROUPED) decode_tile_tab(gt, p.G, NT, BM, L, ti);
+        else decode_tile(p, NT, BM, L, ti);
         gemm_tile_w4p<MODE, A_FLAT, NJ>(p, ti, smem);
     }
 }
@@ -1705,20 +1708,26 @@ hipError_t launch_gemm(int dtype, int mode, const GemmParams& p_in, hipStream_t 
         const long long slots = nj == 2 ? 2 * cus : cus;
         nb = nb < slots ? nb : slots;
         const dim3 grid((unsigned)((nb + 7) / 8 * 8));
-#define MOE_LAUNCH_P(M)                                                                                           \
-    do {                                                                                                          \
-        if (nj == 2) {                                                                                            \
-            if (p.a_bytes > 0) hipLaunchKernelGGL((k_gemm_bf16_w4p<M, false, 2>), grid, dim3(256), 0, s, p, NTp); \
-            else hipLaunchKernelGGL((k_gemm_bf16_w4p<M, true, 2>), grid, dim3(256), 0, s, p, NTp);               \
-        } else {                                                                                                  \
-            if (p.a_bytes > 0) hipLaunchKernelGGL((k_gemm_bf16_w4p<M, false>), grid, dim3(256), 0, s, p, NTp);   \
-            else hipLaunchKernelGGL((k_gemm_bf16_w4p<M, true>), grid, dim3(256), 0, s, p, NTp);                   \
-        }                                                                                                         \
+#define MOE_LAUNCH_P4(M, NJ, GR)                                                                                   \
+    do {                                                                                                           \
+        if (p.a_bytes > 0) hipLaunchKernelGGL((k_gemm_bf16_w4p<M, false, NJ, GR>), grid, dim3(256), 0, s, p, NTp); \
+        else hipLaunchKernelGGL((k_gemm_bf16_w4p<M, true, NJ, GR>), grid, dim3(256), 0, s, p, NTp);                \
+    } while (0)
+#define MOE_LAUNCH_P(M)                                         \
+    do {                                                        \
+        if (p.offsets) {                                        \
+            if (nj == 2) MOE_LAUNCH_P4(M, 2, true);             \
+            else MOE_LAUNCH_P4(M, 4, true);                     \
+        } else {                                                \
+            if (nj == 2) MOE_LAUNCH_P4(M, 2, false);            \
+            else MOE_LAUNCH_P4(M, 4, false);                    \
+        }                                                       \
     } while (0)
         if (mode == GM_UP_SWIGLU) MOE_LAUNCH_P(GM_UP_SWIGLU);
         else if (mode == GM_UP_RELU) MOE_LAUNCH_P(GM_UP_RELU);
         else MOE_LAUNCH_P(GM_DOWN);
 #undef MOE_LAUNCH_P
+#undef MOE_LAUNCH_P4
         return hipGetLastError();
     }
     long long mt;  // upper bound of the m-tile count (grouped: sum of ceil(rows_g / BM) <= R / BM + G)
