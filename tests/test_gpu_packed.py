@@ -33,6 +33,9 @@ VARIANTS = {
                                 I=256, T=24),
     "many_experts": RAGGED.with_(name="packed_many_experts", T=200, N_r=600, K_r=12, Ks=1, I=64, H=256),
     "no_shared": RAGGED.with_(name="packed_no_shared", Ks=0, K_r=5),
+    # 500 dense rows x I=2048: 16 x 16 = 256 of the 32-row shared tiles, so the dense GEMMs take the
+    # four-wave decode tile (fewer would take the one-wave one)
+    "dense_four_wave": RAGGED.with_(name="packed_dense_four_wave", T=500, H=256, I=2048, K_r=2, Ks=1),
 }
 
 
