@@ -315,7 +315,7 @@ int moe_dispatch(const moe_shape* s, const int32_t* topk_idx, int32_t* offsets, 
     hipStream_t st = (hipStream_t)stream;
     rc = do_dispatch(s, topk_idx, offsets, row_token, pair_row, at<int32_t>(ws, L.chunks), st);
     if (rc != MOE_OK) return rc;
-    if (x_perm) MOE_TRY(MOE_PROF_DISPATCH, st, moe::launch_gather(s->dtype, u, row_token, (int)R, s->H, x_perm, st));
+    if (x_perm) MOE_TRY(MOE_PROF_DISPATCH, st, moe::launch_gather(s->dtype, u, row_token, s->T, (int)R, s->H, x_perm, st));
     return MOE_OK;
 }
 

@@ -224,13 +224,16 @@ __global__ __launch_bounds__(256) void k_dispatch1(const int32_t* __restrict__ i
     }
 }
 
+// x_perm[r] = u[row_token[r]].  Rows past the last segment (pairs skipped for an out-of-range expert id)
+// hold whatever the caller's row_token buffer held: every token index is clamped into [0, T), so the
+// gather never reads outside u.
 template <typename E>
 __global__ __launch_bounds__(256) void k_gather(const E* __restrict__ u, const int32_t* __restrict__ row_token,
-                                                int R, int H, E* __restrict__ x_perm) {
+                                                int T, int R, int H, E* __restrict__ x_perm) {
     // one row per workgroup, 16-byte vectors
     const int r = blockIdx.x;
     if (r >= R) return;
-    const int t = row_token[r];
+    const int t = min(max(row_token[r], 0), T - 1);
     const uint4* src = reinterpret_cast<const uint4*>(u + (size_t)t * H);
     uint4* dst = reinterpret_cast<uint4*>(x_perm + (size_t)r * H);
     const int nv = H * (int)sizeof(E) / 16;
@@ -267,14 +270,14 @@ hipError_t launch_dispatch1(const int32_t* idx, int T, int K, int N, int32_t* of
     return hipGetLastError();
 }
 
-hipError_t launch_gather(int dtype, const void* u, const int32_t* row_token, int R, int H, void* x_perm,
+hipError_t launch_gather(int dtype, const void* u, const int32_t* row_token, int T, int R, int H, void* x_perm,
                          hipStream_t s) {
-    if (R == 0) return hipSuccess;
+    if (R == 0 || T == 0) return hipSuccess;
     if (dtype == 0)
-        hipLaunchKernelGGL(k_gather<float>, dim3(R), dim3(256), 0, s, (const float*)u, row_token, R, H,
+        hipLaunchKernelGGL(k_gather<float>, dim3(R), dim3(256), 0, s, (const float*)u, row_token, T, R, H,
                            (float*)x_perm);
     else
-        hipLaunchKernelGGL(k_gather<uint16_t>, dim3(R), dim3(256), 0, s, (const uint16_t*)u, row_token, R, H,
+        hipLaunchKernelGGL(k_gather<uint16_t>, dim3(R), dim3(256), 0, s, (const uint16_t*)u, row_token, T, R, H,
                            (uint16_t*)x_perm);
     return hipGetLastError();
 }

@@ -37,7 +37,8 @@ hipError_t launch_scatter(const int32_t* idx, int T, int K, int N, const int32_t
 // all of the above for one chunk (1 <= T <= kChunk, K >= 1) in one launch
 hipError_t launch_dispatch1(const int32_t* idx, int T, int K, int N, int32_t* offsets, int32_t* row_token,
                             int32_t* pair_row, hipStream_t s);
-hipError_t launch_gather(int dtype, const void* u, const int32_t* row_token, int R, int H, void* x_perm,
+// x_perm [R, H] = u [T, H] rows row_token[r], each index clamped into [0, T)
+hipError_t launch_gather(int dtype, const void* u, const int32_t* row_token, int T, int R, int H, void* x_perm,
                          hipStream_t s);
 
 // ---------------------------------------------------------------- expert FFN (grouped GEMM)

@@ -15,6 +15,11 @@ BF16_FRO, BF16_MAX = 5e-3, 2e-2
 F32_FRO = 1e-5
 
 
+# one line per compared output (label, relative Frobenius, max abs / rms, near ties), printed at the
+# end of the session by tests/conftest.py
+RESULTS = []
+
+
 def say(*a):
     print(*a, flush=True)
     sys.stdout.flush()
@@ -106,6 +111,7 @@ def check_close(got, ref, dtype, label="", output_rounding=False):
     den = np.linalg.norm(ref)
     fro = np.linalg.norm(got - ref) / max(den, 1e-300)
     if dtype == synth.DT_F32:
+        RESULTS.append({"label": label, "n": int(ref.shape[0]) if ref.ndim else 0, "fro": fro, "max_over_rms": None})
         assert fro <= F32_FRO, "%s: rel Frobenius %g > %g" % (label, fro, F32_FRO)
     else:
         rms = den / np.sqrt(max(ref.size, 1))
@@ -114,6 +120,8 @@ def check_close(got, ref, dtype, label="", output_rounding=False):
         excess = (err - allow).max() if ref.size else -1.0
         mx = err.max() if ref.size else 0.0
         say("[check] %s: rel Frobenius %.3e, max abs %.3e = %.4f rms" % (label, fro, mx, mx / max(rms, 1e-300)))
+        RESULTS.append({"label": label, "n": int(ref.shape[0]) if ref.ndim else 0, "fro": fro,
+                        "max_over_rms": mx / max(rms, 1e-300)})
         assert fro <= BF16_FRO, "%s: rel Frobenius %g > %g" % (label, fro, BF16_FRO)
         assert excess <= 0.0, "%s: max abs %g beyond %g * rms %g%s" % (
             label, mx, BF16_MAX, rms, " + 2^-8 |ref|" if output_rounding else "")
@@ -132,8 +140,35 @@ def sample_tokens(T, n, seed=7):
     return np.array(sorted(s), dtype=np.int64)
 
 
-def layer_parity(case, tokens=None, route_all=True, label=""):
-    """Run the layer on the GPU and compare with the oracle. Returns a dict of stats."""
+def cover_routed_tiles(sel, N_r, tokens, tile=128):
+    """tokens, extended so that every m-tile of `tile` rows of every routed expert segment (the rows
+    of the grouped GEMMs, ordered by expert, then by (token, slot)) holds a row of a listed token.
+    Returns (sorted token ids, number of m-tiles, number added)."""
+    offsets, row_token, _ = oracle.dispatch(sel, N_r)
+    have = np.zeros(sel.shape[0], dtype=bool)
+    have[np.asarray(tokens, dtype=np.int64)] = True
+    n_tiles = added = 0
+    for e in range(N_r):
+        for r0 in range(int(offsets[e]), int(offsets[e + 1]), tile):
+            rows = row_token[r0:min(r0 + tile, int(offsets[e + 1]))]
+            n_tiles += 1
+            if not have[rows].any():
+                have[rows[0]] = True
+                added += 1
+    return np.nonzero(have)[0].astype(np.int64), n_tiles, added
+
+
+def strided_tokens(T, stride):
+    """Every stride-th token (0, stride, ...) and the last one."""
+    return np.unique(np.concatenate([np.arange(0, T, stride), [T - 1]])).astype(np.int64)
+
+
+def layer_parity(case, tokens=None, route_all=True, label="", cover_tiles=False):
+    """Run the layer on the GPU and compare with the oracle. Returns a dict of stats.
+
+    tokens: the token ids whose outputs are compared (None = all).  cover_tiles: extend them so that
+    every 128-row m-tile of every routed expert segment holds a compared row.  The MoE-only part
+    (run with MOE_FLAG_NO_RESIDUAL) is compared with the oracle's output minus u, formed in fp64."""
     import torch
     import fine_grained_shared_amd as moe
     w = case.w
@@ -152,13 +187,19 @@ def layer_parity(case, tokens=None, route_all=True, label=""):
         sel_o, g_o, gap = oracle.route(s, case.inp["u"], case.inp["centroids"], case.inp["bias"], tokens=rt)
         rows = slice(None) if rt is None else rt
         stats["near_ties"] = check_routing(sel_gpu[rows], w_gpu[rows], sel_o, g_o, gap, label)
-    tok = np.arange(w.T) if tokens is None else tokens
+    tok = np.arange(w.T) if tokens is None else np.asarray(tokens, dtype=np.int64)
+    if cover_tiles and w.K_r > 0 and tokens is not None:
+        tok, n_tiles, added = cover_routed_tiles(sel_gpu, w.N_r, tok)
+        stats["routed_m_tiles"], stats["tokens_added_for_tiles"] = n_tiles, added
+    stats["tokens_checked"] = int(len(tok))
     say("[parity] %s: oracle layer on %d tokens" % (label or w.name, len(tok)))
     forced = sel_gpu[tok] if w.K_r > 0 else None
     ref, _, _, _ = oracle.layer(s, case.inp, tokens=tok, forced_sel=forced)
-    ref_moe, _, _, _ = oracle.layer(s, case.inp, tokens=tok, forced_sel=forced, residual=False)
+    ref_moe = ref - synth.as_float64(case.inp["u"][tok], w.dtype)
     stats["fro_out"] = check_close(to_f64(out)[tok], ref, w.dtype, label + " out")
     stats["fro_moe"] = check_close(to_f64(moe_part)[tok], ref_moe, w.dtype, label + " moe part",
                                    output_rounding=True)
     say("[parity] %s: ok %s" % (label or w.name, stats))
+    for r in RESULTS[-2:]:
+        r["near_ties"] = stats.get("near_ties")
     return stats, (out, idx, wts)

@@ -1,12 +1,14 @@
 """GPU parity at the high-sparsity shape (H=2048, 1 shared + 512 routed, top-10, I=512, Zipf(1.1)
-centroid norms, sigmoid+bias): prefill T=32768 and the T=64 decode slice."""
+centroid norms, sigmoid+bias): prefill T=32768 (routing on every token, outputs on every 8th token,
+extended so that every 128-row m-tile of every routed expert segment holds a checked row) and the T=64
+decode slice (every token)."""
 import gc
 
 import numpy as np
 import pytest
 
 import synth
-from parity_util import Case, layer_parity, sample_tokens, say
+from parity_util import Case, layer_parity, say, strided_tokens
 
 pytestmark = pytest.mark.gpu
 
@@ -25,7 +27,10 @@ def c4():
 
 def test_c4_prefill_skewed_loads(c4):
     w = c4.w
-    stats, (out, idx, wts) = layer_parity(c4, tokens=sample_tokens(w.T, 96), route_all=True, label="c4p")
+    stats, (out, idx, wts) = layer_parity(c4, tokens=strided_tokens(w.T, 8), route_all=True, label="c4p",
+                                          cover_tiles=True)
+    say("[c4] checked %d tokens over %d routed m-tiles (%d added)" % (
+        stats["tokens_checked"], stats["routed_m_tiles"], stats["tokens_added_for_tiles"]))
     c = np.bincount(idx.cpu().numpy().reshape(-1), minlength=w.N_r)
     nz = c[c > 0]
     say("[c4] near ties %d, empty %d, max/mean %.1f, max/min nonzero %.1f" % (

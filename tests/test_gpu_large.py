@@ -4,10 +4,11 @@
 The projections that read the activations (routed and shared up) cannot use 32-bit buffer
 offsets there and run on the 128 x 512 kernel with 64-bit addressing and direct-to-LDS loads;
 the down projections (the shared one with the fused combine) read the 156 MB / 78 MB hidden
-activations and stay on the buffer-load kernel.  The layer output is checked on a sample of
-tokens against the oracle, routing on the same sample.  With the routed banks packed
-(fragment order), the routed up projection takes the packed kernel's 64-bit-address variant;
-its output must be bit-identical to the unpacked layer's.
+activations and stay on the buffer-load kernel.  Routing is checked on every token; the layer
+output on every 16th token, extended so that every 128-row m-tile of the routed segments holds a
+checked row.  With the routed banks and the shared gate/up bank packed (fragment order), the routed
+and the shared up projections take the packed kernel's 64-bit-address variants (grouped and dense);
+the output must be bit-identical to the unpacked layer's.
 """
 import gc
 
@@ -15,7 +16,7 @@ import numpy as np
 import pytest
 
 import synth
-from parity_util import Case, layer_parity, sample_tokens, say
+from parity_util import Case, layer_parity, say, strided_tokens
 
 pytestmark = pytest.mark.gpu
 
@@ -30,19 +31,21 @@ def test_activations_beyond_2gib():
     say("[large] generating %.2f GB of activations" % (w.T * w.H * 2 / 1e9))
     case = Case(w)
     try:
-        _, (out, idx, _) = layer_parity(case, tokens=sample_tokens(w.T, 48), route_all=False, label="big_u")
+        _, (out, idx, _) = layer_parity(case, tokens=strided_tokens(w.T, 16), route_all=True, label="big_u",
+                                        cover_tiles=True)
         import fine_grained_shared_amd as moe
         pcase = Case.__new__(Case)
         pcase.w, pcase.inp = case.w, case.inp
         pcase.dev = dict(case.dev)
         pcase.dev["w1"] = moe.pack_weights(case.dev["w1"])
         pcase.dev["w2"] = moe.pack_weights(case.dev["w2"])
-        pcase.extra_flags = moe.MOE_FLAG_PACKED_WEIGHTS
+        pcase.dev["w1_sh"] = moe.pack_weights(case.dev["w1_sh"])
+        pcase.extra_flags = moe.MOE_FLAG_PACKED_WEIGHTS | moe.MOE_FLAG_PACKED_SHARED_UP
         pout, pidx, _ = pcase.forward()
         torch.cuda.synchronize()
         assert torch.equal(idx, pidx)
         assert torch.equal(out.view(torch.int16), pout.view(torch.int16)), "packed layer differs"
-        say("[large] packed routed banks: bit-identical")
+        say("[large] packed routed banks and shared up bank: bit-identical")
         pcase.dev.clear()
     finally:
         case.dev.clear()

@@ -8,7 +8,7 @@ import pytest
 
 import oracle
 import synth
-from parity_util import (Case, check_close, check_routing, gpu_shape, layer_parity, sample_tokens, say, to_dev,
+from parity_util import (Case, check_close, check_routing, gpu_shape, layer_parity, say, to_dev,
                          to_f64)
 from synth import (ACT_RELU_BIAS, ACT_SWIGLU, DT_BF16, DT_F32, GATE_SIGMOID_BIAS_NORM, GATE_SOFTMAX,
                    GATE_SOFTMAX_RENORM, Workload)
@@ -54,6 +54,51 @@ def test_c0_tiny_fp32_layer_every_token(torch_cuda):
     assert stats["fro_out"] <= 1e-5
 
 
+def test_c0_coarse_layer_equals_its_fine_split(torch_cuda):
+    """llm-infra-atlas 02, section 2.1 (Eq. 6-8, iso-parameter / iso-FLOP split): the tiny fp32 layer's
+    geometry, a coarse N=4, M=256, top-1 ReLU layer with one shared expert of width 256, run on the GPU
+    next to its m=4 split (16 routed experts of width 64, top-4; four shared experts of width 64).
+    Each slice keeps its coarse expert's centroid, so the four slices of the chosen coarse expert tie and
+    are all selected, each with a quarter of the coarse softmax weight; their down projections are
+    scaled by m (a power of two, exact).  The shared expert is split into four of width 64 with
+    weight 1 (the sum of the slices is the coarse FFN).  Both GPU outputs must agree within the fp32 bar
+    and each must match the oracle."""
+    import fine_grained_shared_amd as moe
+    torch = torch_cuda
+    T, H, N, M, m = 64, 128, 4, 256, 4
+    wc = Workload("c0_coarse", "coarse N=4 M=256 top-1 ReLU layer", T, H, N, 1, 1, M, GATE_SOFTMAX, ACT_RELU_BIAS,
+                  DT_F32)
+    ci = synth.make_inputs(wc)
+    ci["b1"] = synth.normal(8, (N, M), 0.2, DT_F32)
+    ci["b1_sh"] = synth.normal(8, (1, M), 0.2, DT_F32, offset=N * M)
+    iw = M // m
+    fi = dict(ci)
+    fi["centroids"] = np.repeat(ci["centroids"], m, axis=0)
+    fi["w1"] = np.ascontiguousarray(ci["w1"].reshape(N * m, iw, H))
+    fi["b1"] = np.ascontiguousarray(ci["b1"].reshape(N * m, iw))
+    fi["w2"] = np.ascontiguousarray(
+        (ci["w2"].reshape(N, H, m, iw).transpose(0, 2, 1, 3) * np.float32(m)).reshape(N * m, H, iw))
+    fi["w1_sh"] = np.ascontiguousarray(ci["w1_sh"].reshape(m, iw, H))
+    fi["b1_sh"] = np.ascontiguousarray(ci["b1_sh"].reshape(m, iw))
+    fi["w2_sh"] = np.ascontiguousarray(ci["w2_sh"].reshape(H, m, iw).transpose(1, 0, 2))
+    wf = wc.with_(name="c0_fine", N_r=N * m, K_r=m, Ks=m, I=iw)
+    coarse, fine = Case(wc, ci), Case(wf, fi)
+    out_c, idx_c, w_c = coarse.forward()
+    out_f, idx_f, w_f = fine.forward()
+    torch.cuda.synchronize()
+    sel_c, sel_f = idx_c.cpu().numpy(), idx_f.cpu().numpy()
+    assert np.array_equal(sel_f, sel_c * m + np.arange(m)), "the fine layer must take the coarse expert's slices"
+    np.testing.assert_allclose(w_f.cpu().numpy(), np.repeat(w_c.cpu().numpy(), m, axis=1) / m, rtol=1e-6)
+    got_c, got_f = to_f64(out_c), to_f64(out_f)
+    rel = np.linalg.norm(got_f - got_c) / np.linalg.norm(got_c)
+    rel_moe = np.linalg.norm(got_f - got_c) / np.linalg.norm(got_c - synth.as_float64(ci["u"], DT_F32))
+    say("[c0 split] GPU coarse vs fine: rel Frobenius %.3e (MoE part %.3e)" % (rel, rel_moe))
+    assert rel <= 1e-5 and rel_moe <= 1e-5
+    for case, label in ((coarse, "c0 coarse"), (fine, "c0 fine")):
+        stats, _ = layer_parity(case, label=label)
+        assert stats["fro_out"] <= 1e-5
+
+
 @pytest.mark.parametrize("name", list(VARIANTS))
 def test_layer_variants_every_token(torch_cuda, name):
     case = Case(VARIANTS[name])
@@ -61,11 +106,10 @@ def test_layer_variants_every_token(torch_cuda, name):
 
 
 @pytest.mark.parametrize("name", ["c1a", "c1b", "c1b_iso", "c2"])
-def test_layer_configs_sampled(torch_cuda, name):
+def test_layer_configs_every_token(torch_cuda, name):
     w = synth.WORKLOADS[name]
     case = Case(w)
-    toks = sample_tokens(w.T, 96)
-    stats, (out, idx, wts) = layer_parity(case, tokens=toks, label=name)
+    stats, (out, idx, wts) = layer_parity(case, label=name)
     # load histogram of the realised routing (c2: the 8 hot experts draw more tokens)
     counts = np.bincount(idx.cpu().numpy().reshape(-1), minlength=w.N_r)
     say("[parity] %s: load max/mean %.2f, empty %d" % (name, counts.max() / counts.mean(), (counts == 0).sum()))
@@ -97,6 +141,43 @@ def test_stage_route(ragged, torch_cuda):
     key = sc + ragged.inp["bias"].astype(np.float64)
     kk = np.take_along_axis(key, idx.cpu().numpy().astype(np.int64), axis=1)
     assert np.all(np.diff(kk, axis=1) <= 1e-6)
+
+
+def test_dispatch_gather_with_skipped_entries(torch_cuda):
+    """Entries outside [0, N_r) are skipped by the dispatch: those pairs get no row, and the rows past
+    the last segment keep whatever the caller's buffer held.  The x_perm gather clamps every row's
+    token index into [0, T), so it reads only u; the kept pairs' rows are exact."""
+    import fine_grained_shared_amd as moe
+    torch = torch_cuda
+    T, N, K, H = 40, 8, 3, 64
+    rng = np.random.default_rng(11)
+    idx_np = np.stack([rng.permutation(N)[:K] for _ in range(T)]).astype(np.int32)
+    idx_np[3, 1] = -1
+    idx_np[17, 0] = N
+    idx_np[29, 2] = 1 << 30
+    s = moe.make_shape(T, H, N, K, 0, 64, synth.GATE_SOFTMAX, synth.ACT_SWIGLU, synth.DT_BF16)
+    ws = moe.workspace(s)
+    u = torch.randn((T, H), generator=torch.Generator().manual_seed(4)).bfloat16().cuda()
+    R = T * K
+    offsets = torch.full((N + 1,), -7, dtype=torch.int32, device="cuda")
+    row_token = torch.full((R,), -1000000, dtype=torch.int32, device="cuda")   # unwritten rows: far out of range
+    pair_row = torch.full((R,), -7, dtype=torch.int32, device="cuda")
+    x_perm = torch.zeros((R, H), dtype=torch.bfloat16, device="cuda")
+    moe.moe_dispatch(s, torch.from_numpy(idx_np).cuda(), offsets, row_token, pair_row, u, x_perm, ws)
+    torch.cuda.synchronize()
+    off = offsets.cpu().numpy()
+    kept = (idx_np >= 0) & (idx_np < N)
+    assert off[N] == kept.sum() == R - 3
+    # the kept pairs, ordered by expert, then by (token, slot)
+    flat = idx_np.reshape(-1)
+    order = np.argsort(np.where(kept.reshape(-1), flat, N), kind="stable")[:off[N]]
+    rt = row_token.cpu().numpy()
+    assert np.array_equal(rt[:off[N]], order // K)
+    assert np.array_equal(off[:N], np.concatenate([[0], np.cumsum(np.bincount(flat[kept.reshape(-1)],
+                                                                              minlength=N))[:-1]]))
+    xp = x_perm.cpu()
+    assert torch.equal(xp[:off[N]], u.cpu()[torch.from_numpy(rt[:off[N]]).long()])
+    assert torch.equal(xp[off[N]:], u.cpu()[torch.zeros(R - off[N], dtype=torch.long)])   # clamped to token 0
 
 
 def test_stage_dispatch_bit_exact(ragged, torch_cuda):

@@ -1,8 +1,10 @@
 """GPU parity at the full V3-style shape (H=7168, 1 shared + 256 routed, top-8, I=2048, sigmoid+bias).
 
-Prefill T=16384: routing checked on every token, the layer output on a sample of tokens
-(tokens are independent, so a sample is exact for those rows).  Decode T=128: the first 128
-tokens of the same inputs, in the same launch configuration as the bench.
+Prefill T=16384: routing checked on every token; the layer output on every 8th token (2048), extended
+so that every 128-row m-tile of every routed expert segment holds a checked row (tokens are
+independent, so the check is exact for those rows; every 8th token also puts 16 checked rows in each
+128-row tile of the shared down GEMM with the fused combine).  Decode T=128: the first 128 tokens of
+the same inputs, all of them checked, in the same launch configuration as the bench.
 """
 import gc
 
@@ -10,7 +12,7 @@ import numpy as np
 import pytest
 
 import synth
-from parity_util import Case, layer_parity, sample_tokens, say
+from parity_util import Case, layer_parity, say, strided_tokens
 
 pytestmark = pytest.mark.gpu
 
@@ -35,14 +37,17 @@ def load_stats(idx, N):
 
 def test_v3_prefill(v3):
     w = v3.w
-    stats, (out, idx, wts) = layer_parity(v3, tokens=sample_tokens(w.T, 48), route_all=True, label="c3p")
+    stats, (out, idx, wts) = layer_parity(v3, tokens=strided_tokens(w.T, 8), route_all=True, label="c3p",
+                                          cover_tiles=True)
     ls = load_stats(idx, w.N_r)
-    say("[v3] prefill near ties %d, load %s" % (stats["near_ties"], ls))
+    say("[v3] prefill near ties %d, load %s, checked %d tokens over %d routed m-tiles (%d added)" % (
+        stats["near_ties"], ls, stats["tokens_checked"], stats["routed_m_tiles"], stats["tokens_added_for_tiles"]))
     assert ls["empty"] < w.N_r
+    assert stats["tokens_checked"] >= w.T // 8
 
 
 def test_v3_decode(v3):
     case = v3.with_tokens(128)
     case.w = case.w.with_(name="c3d")
-    stats, (out, idx, wts) = layer_parity(case, tokens=sample_tokens(128, 32), route_all=True, label="c3d")
+    stats, (out, idx, wts) = layer_parity(case, route_all=True, label="c3d")
     say("[v3] decode near ties %d, load %s" % (stats["near_ties"], load_stats(idx, case.w.N_r)))
