@@ -18,7 +18,7 @@ from typing import Optional
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
-MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP, MOE_ERR_SCRATCH = 0, -1, -2, -3, -4, -5
 MOE_GATE_SOFTMAX, MOE_GATE_SIGMOID_BIAS_NORM, MOE_GATE_SOFTMAX_RENORM = 0, 1, 2
 MOE_ACT_RELU_BIAS, MOE_ACT_SWIGLU = 0, 1
 MOE_F32, MOE_BF16 = 0, 1
@@ -31,7 +31,8 @@ PROF_NAMES = ["router", "dispatch", "ffn_up", "ffn_down", "shared_up", "shared_d
 
 # every entry point of include/moe.h
 EXPORTS = ("moe_workspace_size", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_pack_weights",
-           "moe_expert_ffn_packed", "moe_shared_ffn", "moe_combine", "moe_layer_forward", "moe_bias_update",
+           "moe_expert_ffn_packed", "moe_shared_ffn", "moe_combine", "moe_layer_forward",
+           "moe_layer_forward_noalloc", "moe_noalloc_scratch_bytes", "moe_bias_update",
            "moe_status_string", "moe_last_hip_error", "moe_profile_enable", "moe_profile_query")
 
 
@@ -76,6 +77,8 @@ def load() -> ctypes.CDLL:
         "moe_shared_ffn": [sp, vp, vp, vp, vp, vp, vp, sz, vp],
         "moe_combine": [sp, vp, vp, vp, vp, vp, vp, vp],
         "moe_layer_forward": [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, sz, vp],
+        "moe_layer_forward_noalloc": [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp],
+        "moe_noalloc_scratch_bytes": [],
         "moe_bias_update": [sp, vp, f32, vp, vp, vp],
         "moe_status_string": [ctypes.c_int],
         "moe_last_hip_error": [],
@@ -85,7 +88,8 @@ def load() -> ctypes.CDLL:
     for name, args in sig.items():
         fn = getattr(lib, name)
         fn.argtypes = args
-        fn.restype = ctypes.c_char_p if name == "moe_status_string" else ctypes.c_int
+        fn.restype = {"moe_status_string": ctypes.c_char_p,
+                      "moe_noalloc_scratch_bytes": ctypes.c_size_t}.get(name, ctypes.c_int)
     _lib = lib
     return lib
 
@@ -182,6 +186,18 @@ def moe_layer_forward(shape, u, centroids, bias, w1, b1, w2, w1_sh, b1_sh, w2_sh
                                     _ptr(w2), _ptr(w1_sh), _ptr(b1_sh), _ptr(w2_sh), flags, _ptr(out),
                                     _ptr(topk_idx_out), _ptr(topk_w_out), _ptr(ws), _nbytes(ws), _stream(stream)),
            "moe_layer_forward")
+
+
+def moe_layer_forward_noalloc(shape, u, centroids, bias, w1, b1, w2, w1_sh, b1_sh, w2_sh, flags, out,
+                              topk_idx_out, topk_w_out, stream=None):
+    _check(load().moe_layer_forward_noalloc(ctypes.byref(shape), _ptr(u), _ptr(centroids), _ptr(bias), _ptr(w1),
+                                            _ptr(b1), _ptr(w2), _ptr(w1_sh), _ptr(b1_sh), _ptr(w2_sh), flags,
+                                            _ptr(out), _ptr(topk_idx_out), _ptr(topk_w_out), _stream(stream)),
+           "moe_layer_forward_noalloc")
+
+
+def moe_noalloc_scratch_bytes() -> int:
+    return load().moe_noalloc_scratch_bytes()
 
 
 def moe_bias_update(shape, offsets, gamma, bias, counts, stream=None):

@@ -4,6 +4,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
 #include <vector>
 
 #include "../../include/moe.h"
@@ -276,6 +278,44 @@ int do_shared_ffn(const moe_shape* s, const void* x, const void* w1, const float
     return MOE_OK;
 }
 
+int layer_forward(const moe_shape* s, const void* u, const void* centroids, const float* bias, const void* w1,
+                  const float* b1, const void* w2, const void* w1_sh, const float* b1_sh, const void* w2_sh,
+                  int32_t flags, void* out, int32_t* topk_idx_out, float* topk_w_out, void* ws, size_t ws_bytes,
+                  void* stream);
+
+// ---------------------------------------------------------------- library-held scratch
+// moe_layer_forward_noalloc takes its workspace from this array instead of a caller's buffer.  Each GPU
+// the library runs on holds its own copy until the process ends.  Host code never uses the array's name
+// as an address (on the host it is a stand-in, not device memory): the device address is looked up once
+// per device with hipGetSymbolAddress, with that device current, and kept in g_scratch.  Every kernel
+// writes the workspace regions it later reads (nothing has to start at zero), so the array is never
+// cleared; calls that overlap in time on one GPU share it and race.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+int scratch_of_current_device(void** ptr) {
+    int dev = -1;
+    const hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e);
+    if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+    void* p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            const hipError_t r = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (r != hipSuccess) return hip_fail(r);
+            if (!p || ((uintptr_t)p & 255u)) return MOE_ERR_HIP;
+            g_scratch[dev].store(p, std::memory_order_release);
+        }
+    }
+    *ptr = p;
+    return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -392,6 +432,33 @@ int moe_layer_forward(const moe_shape* s, const void* u, const void* centroids, 
                       const float* b1, const void* w2, const void* w1_sh, const float* b1_sh, const void* w2_sh,
                       int32_t flags, void* out, int32_t* topk_idx_out, float* topk_w_out, void* ws, size_t ws_bytes,
                       void* stream) {
+    return layer_forward(s, u, centroids, bias, w1, b1, w2, w1_sh, b1_sh, w2_sh, flags, out, topk_idx_out, topk_w_out,
+                         ws, ws_bytes, stream);
+}
+
+int moe_layer_forward_noalloc(const moe_shape* s, const void* u, const void* centroids, const float* bias,
+                              const void* w1, const float* b1, const void* w2, const void* w1_sh, const float* b1_sh,
+                              const void* w2_sh, int32_t flags, void* out, int32_t* topk_idx_out, float* topk_w_out,
+                              void* stream) {
+    int rc = check_shape(s);
+    if (rc != MOE_OK) return rc;
+    if (layout_of(s).total > kScratchBytes) return MOE_ERR_SCRATCH;
+    void* ws = nullptr;
+    if ((rc = scratch_of_current_device(&ws)) != MOE_OK) return rc;
+    return layer_forward(s, u, centroids, bias, w1, b1, w2, w1_sh, b1_sh, w2_sh, flags, out, topk_idx_out, topk_w_out,
+                         ws, kScratchBytes, stream);
+}
+
+size_t moe_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+}  // extern "C"
+
+namespace {
+
+int layer_forward(const moe_shape* s, const void* u, const void* centroids, const float* bias, const void* w1,
+                  const float* b1, const void* w2, const void* w1_sh, const float* b1_sh, const void* w2_sh,
+                  int32_t flags, void* out, int32_t* topk_idx_out, float* topk_w_out, void* ws, size_t ws_bytes,
+                  void* stream) {
     int rc = check_shape(s);
     if (rc != MOE_OK) return rc;
     if (flags & ~(MOE_FLAG_NO_RESIDUAL | MOE_FLAG_PACKED_WEIGHTS | MOE_FLAG_PACKED_SHARED_UP))
@@ -442,6 +509,10 @@ int moe_layer_forward(const moe_shape* s, const void* u, const void* centroids, 
     return MOE_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
 int moe_bias_update(const moe_shape* s, const int32_t* offsets, float gamma, float* bias, int32_t* counts,
                     void* stream) {
     int rc = check_shape(s);
@@ -460,6 +531,7 @@ const char* moe_status_string(int status) {
         case MOE_ERR_UNSUPPORTED: return "unsupported shape";
         case MOE_ERR_WORKSPACE: return "workspace missing or too small";
         case MOE_ERR_HIP: return "HIP error";
+        case MOE_ERR_SCRATCH: return "shape needs more scratch than the library's static buffer holds";
         default: return "unknown status";
     }
 }

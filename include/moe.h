@@ -53,7 +53,9 @@ typedef enum {
     MOE_ERR_INVALID_ARG = -1, /* a pointer, size or enum is out of contract */
     MOE_ERR_UNSUPPORTED = -2, /* a valid shape this build does not cover (e.g. N_r > 1024) */
     MOE_ERR_WORKSPACE = -3,   /* ws is NULL or smaller than moe_workspace_size() */
-    MOE_ERR_HIP = -4          /* a HIP launch or event call failed */
+    MOE_ERR_HIP = -4,         /* a HIP launch or event call failed */
+    MOE_ERR_SCRATCH = -5      /* moe_layer_forward_noalloc: the shape needs more scratch than the
+                                 library's static buffer (moe_noalloc_scratch_bytes()) holds */
 } moe_status;
 
 /* Gating (scores and gate weights of the routed experts). */
@@ -199,6 +201,26 @@ int moe_layer_forward(const moe_shape* shape, const void* u, const void* centroi
                       const void* w1_sh, const float* b1_sh, const void* w2_sh,
                       int32_t flags, void* out, int32_t* topk_idx_out, float* topk_w_out,
                       void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_layer_forward for callers that cannot allocate device memory or pass a workspace: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.  Same arguments and results
+ * as moe_layer_forward (bit for bit) without ws / ws_bytes: the scratch is a static device array of
+ * moe_noalloc_scratch_bytes() = 64 MiB that the library holds on each GPU it runs on until the process
+ * ends (the V3-style decode step, T = 128, needs about 21 MB).  The array of the current device is used
+ * (make the stream's device current, as for any HIP call).  Calls no allocating routine.
+ *   - A shape whose moe_workspace_size exceeds that size -> MOE_ERR_SCRATCH, nothing enqueued.
+ *   - Every call on one GPU shares that GPU's array, which keeps the last call's contents; every
+ *     kernel writes the scratch it later reads, so nothing needs clearing.  Calls that overlap in time
+ *     on one GPU (different streams, or threads without ordering) race on it: serialise them.
+ */
+int moe_layer_forward_noalloc(const moe_shape* shape, const void* u, const void* centroids, const float* bias,
+                              const void* w1, const float* b1, const void* w2,
+                              const void* w1_sh, const float* b1_sh, const void* w2_sh,
+                              int32_t flags, void* out, int32_t* topk_idx_out, float* topk_w_out, void* stream);
+
+/* Bytes of the static scratch array of moe_layer_forward_noalloc. */
+size_t moe_noalloc_scratch_bytes(void);
 
 /*
  * Aux-loss-free balance controller (ibossgateway chapter 7, section 7.4; llm-infra-atlas 02,
