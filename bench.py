@@ -170,6 +170,114 @@ def rocprof_summary(trace_dir, fetch_dir=None, write_dir=None, out_json=None, do
     return "\n".join(lines), res
 
 
+def _csv_rows(d, pattern):
+    rows = []
+    for f in sorted(glob.glob(os.path.join(d, "**", pattern), recursive=True)):
+        with open(f) as fh:
+            rows.extend(csv.DictReader(fh))
+    return rows
+
+
+def _dispatch_counters(d):
+    """{dispatch id: (kernel name, {counter: value summed over the dispatch's rows})} of a --pmc run."""
+    out = {}
+    for r in _csv_rows(d, "*counter_collection.csv"):
+        did = r.get("Dispatch_Id") or r.get("Correlation_Id")
+        name, vals = out.setdefault(did, (r["Kernel_Name"], {}))
+        vals[r["Counter_Name"]] = vals.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return out
+
+
+def _dispatch_ns(d):
+    """{dispatch id: duration in ns} from the kernel trace written by the same rocprofv3 run."""
+    out = {}
+    for r in _csv_rows(d, "*kernel_trace.csv"):
+        did = r.get("Dispatch_Id") or r.get("Correlation_Id")
+        out[did] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+    return out
+
+
+def _simd_count(d, default=1024):
+    for r in _csv_rows(d, "*agent_info.csv"):
+        for k in ("Simd_Count", "SIMD_Count", "simd_count"):
+            if r.get(k) and r.get("Agent_Type", r.get("Type", "GPU")).upper().endswith("GPU") and float(r[k]) > 0:
+                n = float(r[k])
+                cus = float(r.get("Cu_Count") or r.get("Compute_Unit_Count") or 0)
+                return int(n * cus) if 0 < n <= 8 and cus > 0 else int(n)
+    return default
+
+
+def counter_summary(pmc_dir, fetch_dir=None, write_dir=None, copy_bytes=COPY_BYTES):
+    """Per-kernel table of a rocprofv3 run with --pmc SQ_VALU_MFMA_BUSY_CYCLES MfmaUtil GRBM_GUI_ACTIVE
+    SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_BUSY_CYCLES --kernel-trace, plus optional FETCH_SIZE and WRITE_SIZE runs.
+
+    MFMA busy % is rocprofv3's MfmaUtil: sum over SIMDs of SQ_VALU_MFMA_BUSY_CYCLES / (max over XCDs of
+    GRBM_GUI_ACTIVE x SIMDs).  The shader clock is that max GRBM_GUI_ACTIVE (recovered from the two) over
+    the dispatch's duration.  Executed bf16 MFMA work is SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 FLOP.
+    HBM bytes are FETCH_SIZE and WRITE_SIZE scaled by what they read for the bench's plain 1 GiB device
+    copy (the largest copy-kernel dispatch of the run)."""
+    disp = _dispatch_counters(pmc_dir)
+    dur = _dispatch_ns(pmc_dir)
+    simds = _simd_count(pmc_dir)
+    per = {}
+    for did, (name, v) in disp.items():
+        if did not in dur or dur[did] <= 0:
+            continue
+        a = per.setdefault(_short(name), {"n": 0, "ns": 0.0, "util": 0.0, "clk": 0.0, "mops": 0.0, "clk_n": 0})
+        a["n"] += 1
+        a["ns"] += dur[did]
+        util = v.get("MfmaUtil")
+        busy = v.get("SQ_VALU_MFMA_BUSY_CYCLES")
+        if util is not None:
+            a["util"] += util
+        if util and busy:
+            grbm_max = busy / (util / 100.0 * simds)
+            a["clk"] += grbm_max / dur[did]
+            a["clk_n"] += 1
+        a["mops"] += v.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0)
+    traffic = {}
+    if fetch_dir and write_dir:
+        fc, wc = _read_counters(fetch_dir), _read_counters(write_dir)
+        copy_f = max([x for k, d in fc.items() if "copyBuffer" in k for x in d.get("FETCH_SIZE", [])] or [0])
+        copy_w = max([x for k, d in wc.items() if "copyBuffer" in k for x in d.get("WRITE_SIZE", [])] or [0])
+        if copy_f > 0 and copy_w > 0:
+            sf, sw = copy_bytes / (copy_f * 1024), copy_bytes / (copy_w * 1024)
+            for k in set(fc) | set(wc):
+                f = fc.get(k, {}).get("FETCH_SIZE", [])
+                w = wc.get(k, {}).get("WRITE_SIZE", [])
+                if f and w:
+                    traffic[_short(k)] = (sum(f) / len(f) * 1024 * sf, sum(w) / len(w) * 1024 * sw)
+            traffic["_scales"] = (sf, sw, copy_f, copy_w)
+    lines = ["| kernel | dispatches | avg ms | MFMA busy % | shader clock GHz | executed bf16 TFLOP/s |"
+             " read GB | written GB | HBM TB/s |",
+             "|---|---|---|---|---|---|---|---|---|"]
+    res = {}
+    for k in sorted(per, key=lambda k: -per[k]["ns"]):
+        a = per[k]
+        n = a["n"]
+        ms = a["ns"] / n / 1e6
+        util = a["util"] / n
+        # the counters cover the dispatch plus the profiler's own set-up around it, so the clock is
+        # only meaningful for dispatches far longer than that (here: 0.5 ms and more)
+        clk = a["clk"] / a["clk_n"] if a["clk_n"] and ms >= 0.5 else float("nan")
+        tfs = a["mops"] / n * 512 / (ms * 1e-3) / 1e12
+        rd = wr = tbs = None
+        if k in traffic:
+            rd, wr = traffic[k]
+            tbs = (rd + wr) / (ms * 1e-3) / 1e12
+        res[k] = {"dispatches": n, "avg_ms": ms, "mfma_busy_pct": util, "clock_ghz": clk,
+                  "executed_tflops": tfs, "read_bytes": rd, "write_bytes": wr}
+        lines.append("| %s | %d | %.4f | %.1f | %s | %.0f | %s | %s | %s |" % (
+            k, n, ms, util, "-" if clk != clk else "%.2f" % clk, tfs, "-" if rd is None else "%.3f" % (rd / 1e9),
+            "-" if wr is None else "%.3f" % (wr / 1e9), "-" if tbs is None else "%.2f" % tbs))
+    if "_scales" in traffic:
+        sf, sw, cf, cw = traffic["_scales"]
+        lines.append("")
+        lines.append("Byte scales from the %d-byte device copy: FETCH_SIZE %.0f KiB -> x %.3f, WRITE_SIZE %.0f KiB "
+                     "-> x %.3f.  SIMDs: %d." % (copy_bytes, cf, sf, cw, sw, simds))
+    return "\n".join(lines), res
+
+
 # ---------------------------------------------------------------- timing helpers
 
 def _upload(inp):
@@ -300,11 +408,17 @@ def main():
     ap.add_argument("--pmc-fetch", metavar="DIR")
     ap.add_argument("--pmc-write", metavar="DIR")
     ap.add_argument("--traffic-json", metavar="FILE")
+    ap.add_argument("--counter-summary", metavar="PMC_DIR",
+                    help="per-kernel MFMA busy %%, shader clock and HBM bytes of rocprofv3 --pmc runs, then exit")
     ap.add_argument("--weights", choices=("packed", "unpacked"), default="packed",
                     help="routed expert banks in fragment order (moe_pack_weights, done once when the weights "
                          "are loaded, before timing; the layer's output is bit-identical) or in the [out, in] "
                          "layout")
     args = ap.parse_args()
+    if args.counter_summary:
+        text, _ = counter_summary(args.counter_summary, args.pmc_fetch, args.pmc_write)
+        print(text)
+        return
     if args.rocprof_summary:
         text, _ = rocprof_summary(args.rocprof_summary, args.pmc_fetch, args.pmc_write, args.traffic_json,
                                   dominant_kernel(args.weights == "packed"))
