@@ -374,6 +374,103 @@ def _kernel_times(fn, steps):
     return res
 
 
+def _scrubbed_step_ms(fn, steps, scrub):
+    """Average time of fn over `steps` calls, each after a write over `scrub` (a device buffer larger
+    than the 256 MB last-level cache), with events around fn only: every call starts from cold caches."""
+    import torch
+    st = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        scrub.fill_(i & 0xFF)
+        ev[i][0].record(st)
+        fn()
+        ev[i][1].record(st)
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+
+def _layer_call(w, d, flags, T=None, bias="default"):
+    """A closure running moe_layer_forward on the first T tokens of the uploaded inputs d."""
+    import torch
+    import fine_grained_shared_amd as moe
+    T = w.T if T is None else T
+    shape = moe.make_shape(T, w.H, w.N_r, w.K_r, w.Ks, w.I, w.gating, w.act, w.dtype)
+    ws = moe.workspace(shape)
+    u = d["u"] if T == w.T else d["u"][:T].contiguous()
+    out = torch.empty((T, w.H), dtype=moe.torch_dtype(shape), device="cuda")
+    idx = torch.empty((T, max(w.K_r, 1)), dtype=torch.int32, device="cuda")
+    wts = torch.empty((T, max(w.K_r, 1)), dtype=torch.float32, device="cuda")
+    b = d["bias"] if bias == "default" else bias
+
+    def fn():
+        moe.moe_layer_forward(shape, u, d["centroids"], b, d["w1"], d["b1"], d["w2"], d["w1_sh"], d["b1_sh"],
+                              d["w2_sh"], flags, out, idx, wts, ws)
+    return fn, idx
+
+
+def _pack_all(w, d):
+    """Routed banks and the shared gate/up bank in fragment order (bf16 layers); returns the flags."""
+    import fine_grained_shared_amd as moe
+    if w.dtype != 1:
+        return 0
+    for k in ("w1", "w2") + (("w1_sh",) if w.Ks > 0 else ()):
+        d[k] = moe.pack_weights(d[k])
+    return moe.MOE_FLAG_PACKED_WEIGHTS | (moe.MOE_FLAG_PACKED_SHARED_UP if w.Ks > 0 else 0)
+
+
+def other_workloads(steps, warmup, names=("c1a", "c1b", "c1b_iso", "c2", "c4p")):
+    """The other prefill layers of the workload table, timed like the headline one, and the
+    high-sparsity decode slice (the first 64 tokens of its prefill inputs) with the caches scrubbed
+    before every step (its touched weights, about 0.26 GB, would otherwise stay in the 256 MB
+    last-level cache from one step to the next)."""
+    import torch
+    import synth
+    res = {}
+    for name in names:
+        w = synth.WORKLOADS[name]
+        inp = synth.make_inputs(w)
+        d = _upload(inp)
+        del inp
+        flags = _pack_all(w, d)
+        fn, idx = _layer_call(w, d, flags)
+        ms = _time_steps(fn, steps, warmup)
+        kt = _kernel_times(fn, max(2, min(steps, 10)))
+        fl = layer_flops(w)
+        counts = np.bincount(idx.cpu().numpy().reshape(-1), minlength=w.N_r)
+        res[name] = {"workload": w.desc, "ms_per_step": round(ms, 4), "tokens_per_s": round(w.T / (ms * 1e-3), 1),
+                     "tflops": round(fl / (ms * 1e-3) / 1e12, 2),
+                     "pct_bf16_peak": round(100 * fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+                     "kernels_ms_per_step": {k: round(v["ms_per_step"], 4) for k, v in kt.items()},
+                     "load_max_over_mean": round(float(counts.max() / counts.mean()), 2),
+                     "empty_experts": int((counts == 0).sum())}
+        print("[bench] %s prefill %.3f ms/step, %.1f %% of bf16 peak" % (name, ms, res[name]["pct_bf16_peak"]),
+              file=sys.stderr, flush=True)
+        if name == "c4p":
+            Td = synth.WORKLOADS["c4d"].T
+            wd = w.with_(T=Td)
+            dfn, didx = _layer_call(w, d, flags, T=Td)
+            for _ in range(warmup):
+                dfn()
+            scrub = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+            cold = _scrubbed_step_ms(dfn, max(steps, 10), scrub)
+            warm = _time_steps(dfn, max(steps, 10), warmup)
+            del scrub
+            touched = int(np.unique(didx.cpu().numpy()).size)
+            nb = decode_bytes(wd, touched)
+            res["c4d"] = {"workload": synth.WORKLOADS["c4d"].desc, "ms_per_step": round(cold, 4),
+                          "tokens_per_s": round(Td / (cold * 1e-3), 1), "touched_experts": touched,
+                          "algorithmic_bytes": nb, "GB_per_s": round(nb / (cold * 1e-3) / 1e9, 1),
+                          "pct_hbm_peak": round(100 * nb / (cold * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
+                          "cache": "1 GiB scrub written before every timed step (events around the step only)",
+                          "warm_cache_ms_per_step": round(warm, 4)}
+            print("[bench] c4d decode %.4f ms/step (cold caches), %.4f warm" % (cold, warm), file=sys.stderr,
+                  flush=True)
+        d.clear()
+        torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(w, inp, budget_s=20.0):
     """The fp64 oracle on the host cores, on a bounded sample of the workload's tokens."""
     import oracle
@@ -402,6 +499,7 @@ def main():
     ap.add_argument("--decode-tokens", type=int, default=128)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-other", action="store_true", help="skip the other workloads of the table")
     ap.add_argument("--no-unpacked", action="store_true",
                     help="with packed weights, skip timing the same step on the [out, in] banks")
     ap.add_argument("--rocprof-summary", metavar="TRACE_DIR", help="summarise a rocprofv3 run and exit")
@@ -552,6 +650,22 @@ def main():
                             "copy_GB_per_s": round(copy, 1),
                             "kernels_ms_per_step": {k: round(v["ms_per_step"], 4) for k, v in dkt.items()}}
         print("[bench] decode %.3f ms/step, %.0f GB/s" % (dms, gbs), file=sys.stderr, flush=True)
+        if w.gating == 1:
+            # sensitivity: the selection bias set to 0 (near-uniform routing touches almost every expert)
+            zfn, zidx = _layer_call(w, d, flags, T=Td, bias=None)
+            zms = _time_steps(zfn, max(args.steps, 10), args.warmup)
+            zt = int(np.unique(zidx.cpu().numpy()).size)
+            zb = decode_bytes(wd, zt)
+            result["decode_bias0"] = {"T": Td, "bias": "0 (sensitivity run)", "ms_per_step": round(zms, 4),
+                                      "touched_experts": zt, "algorithmic_bytes": zb,
+                                      "GB_per_s": round(zb / (zms * 1e-3) / 1e9, 1),
+                                      "pct_hbm_peak": round(100 * zb / (zms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2)}
+            print("[bench] decode, bias 0: %.3f ms/step, %d experts" % (zms, zt), file=sys.stderr, flush=True)
+
+    if not args.no_other and args.workload == "c3p":
+        d.clear()
+        torch.cuda.empty_cache()
+        result["other_workloads"] = other_workloads(args.steps, args.warmup)
 
     if not args.no_cpu:
         print("[bench] timing the fp64 oracle on the host cores", file=sys.stderr, flush=True)

@@ -23,8 +23,6 @@
 // choice of kernel does not change a result bit.  For SwiGLU the weight rows of a tile are gate
 // rows and the matching up rows, so the epilogue has both halves of every output element in the
 // same lane.  fp32 path: plain VALU kernels (the tiny fp32 layer only).
-#include <stdlib.h>
-
 #include <type_traits>
 
 #include "common.hpp"
@@ -35,20 +33,6 @@ namespace moe {
 constexpr int BM = 128, BN = 128, BK = 64;
 
 int gemm_bm(int dtype) { return dtype == 0 ? 1 : BM; }
-
-// Wide-tile kernel selection for A/B measurements: MOE_GEMM_WIDE=0 (128 x 128 tiles only),
-// =dma (128 x 512 tiles staged with direct-to-LDS loads); default: 128 x 512 tiles staged through
-// registers with buffer loads (the direct-to-LDS kernel serves operands spanning 2 GiB or more).
-static int wide_mode() {
-    static int v = -1;
-    if (v < 0) {
-        const char* e = getenv("MOE_GEMM_WIDE");
-        v = 2;
-        if (e && e[0] == '0') v = 0;
-        else if (e && e[0] == 'd') v = 1;
-    }
-    return v;
-}
 
 // Compute units of the current device (cached per device id).
 static int device_cus() {
@@ -1741,10 +1725,10 @@ hipError_t launch_gemm(int dtype, int mode, const GemmParams& p_in, hipStream_t 
     // direct-to-LDS kernel: the plain modes, for operands too large for 32-bit buffer offsets.
     // The fused combine stays on the 128 x 128 tiles: its epilogue gathers K_r routed rows per
     // output row, and two workgroups per CU overlap that gather with the other's MFMAs.
-    const bool w4 = wide_mode() == 2 && p.a_bytes > 0 && p.b_bytes > 0;
+    const bool w4 = p.a_bytes > 0 && p.b_bytes > 0;
     // fp32 output (router logits) with whole 512-wide column tiles takes it from one tile per CU on: the
     // 128 x 128 kernel's single-stage k-loop is slower than the wide tile's at any count
-    const bool wide = wide_mode() != 0 && mode != GM_DOWN_COMBINE && (w4 || mode != GM_F32OUT) &&
+    const bool wide = mode != GM_DOWN_COMBINE && (w4 || mode != GM_F32OUT) &&
                       (mt * NTw >= 2 * cus || (mode == GM_F32OUT && p.N % WBN == 0 && mt * NTw >= cus)) &&
                       rows_per_group >= 64;
     if (wide) {

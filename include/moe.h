@@ -15,8 +15,13 @@
  * - Pointers are device memory owned by the caller, row-major, contiguous.
  *   The library never allocates or frees device memory: scratch space comes
  *   from the caller's workspace `ws` of `ws_bytes` bytes (see
- *   moe_workspace_size).  Host pointers: only `shape` (and the out-params of
- *   moe_workspace_size / moe_profile_query).
+ *   moe_workspace_size), or, for moe_layer_forward_noalloc, from a static
+ *   device array the library holds.  Host pointers: only `shape` (and the
+ *   out-params of moe_workspace_size / moe_profile_query).
+ * - Process-wide state: the profiling counters of moe_profile_* (every other
+ *   call only reads whether profiling is on), the last HIP error (per thread)
+ *   and the static scratch of moe_layer_forward_noalloc.  None of it changes
+ *   a result.
  * - `stream` is a hipStream_t (NULL = the default stream).  Every call only
  *   enqueues work on that stream and returns; nothing is read back to the host
  *   and the host never waits.
