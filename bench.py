@@ -455,6 +455,7 @@ def other_workloads(steps, warmup, names=("c1a", "c1b", "c1b_iso", "c2", "c4p"))
             scrub = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
             cold = _scrubbed_step_ms(dfn, max(steps, 10), scrub)
             warm = _time_steps(dfn, max(steps, 10), warmup)
+            dkt = _kernel_times(dfn, 10)
             del scrub
             touched = int(np.unique(didx.cpu().numpy()).size)
             nb = decode_bytes(wd, touched)
@@ -463,7 +464,8 @@ def other_workloads(steps, warmup, names=("c1a", "c1b", "c1b_iso", "c2", "c4p"))
                           "algorithmic_bytes": nb, "GB_per_s": round(nb / (cold * 1e-3) / 1e9, 1),
                           "pct_hbm_peak": round(100 * nb / (cold * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
                           "cache": "1 GiB scrub written before every timed step (events around the step only)",
-                          "warm_cache_ms_per_step": round(warm, 4)}
+                          "warm_cache_ms_per_step": round(warm, 4),
+                          "kernels_ms_per_step": {k: round(v["ms_per_step"], 4) for k, v in dkt.items()}}
             print("[bench] c4d decode %.4f ms/step (cold caches), %.4f warm" % (cold, warm), file=sys.stderr,
                   flush=True)
         d.clear()

@@ -102,7 +102,7 @@ Layout layout_of(const moe_shape* s) {
     };
     const size_t T = (size_t)s->T, R = (size_t)s->T * s->K_r, E = esz(s);
     const size_t nchunk = (T + moe::kChunk - 1) / moe::kChunk;
-    L.logits = take(T * s->N_r * 4 * (moe::logits_split(s->dtype == MOE_BF16 ? 1 : 0, s->T, s->H, s->N_r) ? 2 : 1));
+    L.logits = take(T * s->N_r * 4 * (s->dtype == MOE_BF16 ? moe::logits_groups(s->H) : 1));
     L.topk_idx = take(R * 4);
     L.topk_w = take(R * 4);
     L.offsets = take(((size_t)s->N_r + 1) * 4);
@@ -133,10 +133,10 @@ int check_ws(const moe_shape* s, void* ws, size_t ws_bytes) {
 int do_route(const moe_shape* s, const void* u, const void* e, const float* bias, int32_t* idx, float* w,
              float* logits, hipStream_t st) {
     if (s->T == 0 || s->K_r == 0) return MOE_OK;
-    MOE_TRY(MOE_PROF_ROUTER, st, moe::launch_logits(s->dtype, u, e, logits, s->T, s->H, s->N_r, st));
-    const int split = moe::logits_split(s->dtype == MOE_BF16 ? 1 : 0, s->T, s->H, s->N_r) ? 1 : 0;
-    moe::SelectArgs a{logits, split, bias, s->T, s->N_r, s->K_r, s->gating, s->n_group, s->topk_group,
+    const int groups = s->dtype == MOE_BF16 ? moe::logits_groups(s->H) : 1;
+    moe::SelectArgs a{logits, groups, bias, s->T, s->N_r, s->K_r, s->gating, s->n_group, s->topk_group,
                       s->mask_top_r, idx, w};
+    MOE_TRY(MOE_PROF_ROUTER, st, moe::launch_logits(s->dtype, u, e, logits, s->T, s->H, s->N_r, st));
     MOE_TRY(MOE_PROF_ROUTER, st, moe::launch_select(a, st));
     return MOE_OK;
 }

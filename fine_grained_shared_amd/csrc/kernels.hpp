@@ -7,16 +7,15 @@
 namespace moe {
 
 // ---------------------------------------------------------------- router
-// logits [T, N] fp32 = u [T, H] . centroids [N, H]^T
+// logits = u [T, H] . centroids [N, H]^T in fp32: [T, N] (fp32), or for bf16 the logits_groups(H)
+// partial sums of the fixed summation order side by side, [T, G N]; the selection adds them
 hipError_t launch_logits(int dtype, const void* u, const void* e, float* logits, int T, int H, int N,
                          hipStream_t s);
-// The prefill logits GEMM splits the reduction in two halves (two groups of K/2, written side by side as
-// [T, 2N]) when T is large: the narrow GEMM then has twice the tiles.  k_select adds the halves (first + second).
-bool logits_split(int dtype, int T, int H, int N);
+int logits_groups(int H);
 // per-token scores, selection and gate weights from the logits
 struct SelectArgs {
-    const float* logits;      // [T, N], or [T, 2N] halves when split
-    int split;
+    const float* logits;      // [T, groups N]
+    int groups;               // 1, 2 or 4 partial sums per logit, added in group order
     const float* bias;
     int T, N, K;
     int gating;

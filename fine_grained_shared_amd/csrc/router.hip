@@ -9,105 +9,64 @@
 
 namespace moe {
 
-// ---------------------------------------------------------------- logits, bf16 (MFMA)
-// Tile: TB*16 tokens x 64 experts per workgroup.  Wave w owns experts [e0 + 16 w, +16) and all
-// TB token blocks; v_mfma_f32_16x16x32_bf16 with both operands read straight from global
-// memory as 16-byte rows (u and the centroids are both K-contiguous).
-template <int TB>
-__global__ __launch_bounds__(256) void k_logits_bf16(const uint16_t* __restrict__ u,
-                                                     const uint16_t* __restrict__ e,
-                                                     float* __restrict__ logits, int T, int H, int N) {
-    const int lane = threadIdx.x & 63;
-    const int w = threadIdx.x >> 6;
-    const int t0 = blockIdx.x * (TB * 16);
-    const int e0 = blockIdx.y * 64 + w * 16;
-    if (e0 >= N) return;
-    const int r = lane & 15;
-    const int kq = (lane >> 4) * 8;
-    const uint16_t* ap[TB];
-#pragma unroll
-    for (int b = 0; b < TB; ++b) {
-        int t = min(t0 + b * 16 + r, T - 1);
-        ap[b] = u + (size_t)t * H + kq;
-    }
-    const int ex = min(e0 + r, N - 1);
-    const uint16_t* bp = e + (size_t)ex * H + kq;
-    f32x4 acc[TB];
-#pragma unroll
-    for (int b = 0; b < TB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int k = 0; k < H; k += 32) {
-        uint4 bv = *reinterpret_cast<const uint4*>(bp + k);
-#pragma unroll
-        for (int b = 0; b < TB; ++b) {
-            uint4 av = *reinterpret_cast<const uint4*>(ap[b] + k);
-            acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
-                                                             __builtin_bit_cast(bf16x8, bv), acc[b], 0, 0, 0);
-        }
-    }
-    // D[i][j]: j = lane % 16 (expert), i = 4 * (lane / 16) + q (token)
-    const int col = e0 + r;
-    if (col < N) {
-#pragma unroll
-        for (int b = 0; b < TB; ++b)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                int t = t0 + b * 16 + (lane >> 4) * 4 + q;
-                if (t < T) logits[(size_t)t * N + col] = acc[b][q];
-            }
-    }
-}
+// ---------------------------------------------------------------- logits, bf16
+// Every bf16 logit l[t,i] = u_t . e_i is summed in one fixed order, whatever T is and whichever kernel
+// computes it, so a token's logits - and its routing, near ties included - do not depend on how the
+// tokens are batched:
+//   H is cut into G equal reduction groups - two for long hidden sizes (H >= 4096, H % 128 == 0),
+//   else one - each summed as one fp32 chain of v_mfma_f32_32x32x16_bf16 over its 16-deep k-chunks in
+//   ascending order, with the token in the A operand and the expert in the B operand; the groups are
+//   written side by side as [T, G N] and added by the selection kernel in group order.
+// G depends on the layer's shape only, never on T.  Two groups halve the k-loop of the GEMM's few
+// 128 x 128 tiles (V3-style prefill router 0.165 -> 0.116 ms) and the chain of the small-batch kernel;
+// for H = 2048 one group is faster on both (the partial sums cost traffic: four groups at 512 experts
+// and 32768 tokens would write and re-read 268 MB).
+// That is the order of the tiled GEMM kernels (GM_F32OUT mode), which compute it for many tokens; the
+// kernel below computes it for a few (a decode step) or for expert counts that are not multiples of 64.
+int logits_groups(int H) { return H >= 4096 && H % 128 == 0 ? 2 : 1; }
 
-// ---------------------------------------------------------------- logits, bf16, few tokens
-// Decode-sized T: a workgroup computes 16 tokens x 16 experts; its four waves take contiguous
-// quarters of H and keep eight 32-wide k-chunks of loads in flight (latency, not bandwidth, bounds
-// this shape), then the four partial sums are added in a fixed order through LDS.
-__global__ __launch_bounds__(256) void k_logits_bf16_sk(const uint16_t* __restrict__ u,
-                                                        const uint16_t* __restrict__ e,
-                                                        float* __restrict__ logits, int T, int H, int N) {
-    __shared__ f32x4 part[4][64];
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int r = lane & 15, kq = (lane >> 4) * 8;
-    const int t = min((int)blockIdx.x * 16 + r, T - 1);
-    const int ex = min((int)blockIdx.y * 16 + r, N - 1);
-    const uint16_t* ap = u + (size_t)t * H + kq;
-    const uint16_t* bp = e + (size_t)ex * H + kq;
-    const int nch = H / 32;
-    const int c0 = nch * w / 4, c1 = nch * (w + 1) / 4;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    int c = c0;
-    for (; c + 8 <= c1; c += 8) {
-        uint4 av[8], bv[8];
+// One wave per 32 tokens x 32 experts of one reduction group: the chain of its k-chunks, operands loaded
+// from global memory sixteen chunks ahead (latency bounds this shape: the more bytes in flight per wave,
+// the faster).  Lane l feeds row l % 32 (token for A, expert for B) and the k-half l / 32 of each
+// 16-deep chunk, as the tiled kernels do.
+__global__ __launch_bounds__(64) void k_logits_bf16_dec(const uint16_t* __restrict__ u, const uint16_t* __restrict__ e,
+                                                        float* __restrict__ logits, int T, int H, int N, int G) {
+    const int lane = threadIdx.x;
+    const int g = blockIdx.z, Kg = H / G;
+    const int t = min((int)blockIdx.x * 32 + (lane & 31), T - 1);
+    const int ex = min((int)blockIdx.y * 32 + (lane & 31), N - 1);
+    const uint16_t* ap = u + (size_t)t * H + (size_t)g * Kg + (lane >> 5) * 8;
+    const uint16_t* bp = e + (size_t)ex * H + (size_t)g * Kg + (lane >> 5) * 8;
+    const int nc = Kg / 16;
+    f32x16 acc;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            av[j] = *reinterpret_cast<const uint4*>(ap + (c + j) * 32);
-            bv[j] = *reinterpret_cast<const uint4*>(bp + (c + j) * 32);
-        }
+    for (int q = 0; q < 16; ++q) acc[q] = 0.f;
+    constexpr int D = 16;   // chunks in flight
+    uint4 av[D], bv[D];
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[j]),
-                                                          __builtin_bit_cast(bf16x8, bv[j]), acc, 0, 0, 0);
+    for (int j = 0; j < D; ++j) {
+        const int c = min(j, nc - 1);
+        av[j] = *reinterpret_cast<const uint4*>(ap + c * 16);
+        bv[j] = *reinterpret_cast<const uint4*>(bp + c * 16);
     }
-    for (; c < c1; ++c) {
-        const uint4 av = *reinterpret_cast<const uint4*>(ap + c * 32);
-        const uint4 bv = *reinterpret_cast<const uint4*>(bp + c * 32);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, bv),
-                                                      acc, 0, 0, 0);
-    }
-    part[w][lane] = acc;
-    __syncthreads();
-    if (w == 0) {
-        f32x4 v = part[0][lane];
+    for (int c0 = 0; c0 < nc; c0 += D) {
 #pragma unroll
-        for (int q = 1; q < 4; ++q) v += part[q][lane];
-        // D[i][j]: j = lane % 16 (expert), i = 4 * (lane / 16) + q (token)
-        const int col = blockIdx.y * 16 + r;
-        if (col < N) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int tt = blockIdx.x * 16 + (lane >> 4) * 4 + q;
-                if (tt < T) logits[(size_t)tt * N + col] = v[q];
-            }
+        for (int j = 0; j < D; ++j) {
+            if (c0 + j < nc)
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[j]),
+                                                              __builtin_bit_cast(bf16x8, bv[j]), acc, 0, 0, 0);
+            const int c = min(c0 + D + j, nc - 1);   // the next round's chunk (clamped: re-read, unused)
+            av[j] = *reinterpret_cast<const uint4*>(ap + c * 16);
+            bv[j] = *reinterpret_cast<const uint4*>(bp + c * 16);
         }
+    }
+    // D[i][j] of the 32 x 32 block: j = lane % 32 (expert), i = 8 (q / 4) + 4 (lane / 32) + q % 4 (token)
+    const int col = blockIdx.y * 32 + (lane & 31);
+    if (col >= N) return;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+        const int tt = blockIdx.x * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+        if (tt < T) logits[(size_t)tt * G * N + (size_t)g * N + col] = acc[q];
     }
 }
 
@@ -124,12 +83,6 @@ __global__ __launch_bounds__(256) void k_logits_f32(const float* __restrict__ u,
     logits[idx] = acc;
 }
 
-// Below 32768 tokens the 128 x 128 tiles of the logits GEMM (T / 128 x N / 128 of them) leave half of
-// its two-workgroups-per-CU slots empty; two reduction halves fill them.
-bool logits_split(int dtype, int T, int H, int N) {
-    return dtype != 0 && T >= 1024 && T < 32768 && N % 64 == 0 && H % 128 == 0;
-}
-
 hipError_t launch_logits(int dtype, const void* u, const void* e, float* logits, int T, int H, int N,
                          hipStream_t s) {
     if (T == 0 || N == 0) return hipSuccess;
@@ -137,43 +90,37 @@ hipError_t launch_logits(int dtype, const void* u, const void* e, float* logits,
         long long n = (long long)T * N;
         hipLaunchKernelGGL(k_logits_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, (const float*)u,
                            (const float*)e, logits, T, H, N);
-    } else if (T >= 1024 && N % 64 == 0) {
-        // prefill: the tiled MFMA GEMM (LDS-staged, fp32 output) over u [T, H] x e [N, H]^T; split, the
-        // two halves of H are two dense groups writing [T, 2N] side by side
-        const bool split = logits_split(dtype, T, H, N);
+        return hipGetLastError();
+    }
+    const int G = logits_groups(H);
+    // The two kernels give the same bits, so the choice is by speed only: the tiled GEMM once its 128 x 128
+    // output tiles fill the GPU, else the small-batch kernel (many more, shorter waves).
+    const long long gemm_tiles = (long long)((T + 127) / 128) * ((N + 127) / 128) * G;
+    if (T >= 1024 && N % 64 == 0 && gemm_tiles >= 256) {
+        // many tokens: the tiled MFMA GEMM (fp32 output) over u [T, H] x e [N, H]^T, the reduction groups
+        // as dense groups writing [T, G N] side by side
         GemmParams p{};
         p.A = u;
         p.lda = H;
         p.a_nrows = T;
         p.B = e;
         p.ldb = H;
-        p.K = split ? H / 2 : H;
+        p.K = H / G;
         p.Kseg = p.K;
-        p.sA_group = split ? H / 2 : 0;
-        p.sB_group = split ? H / 2 : 0;
+        p.sA_group = H / G;
+        p.sB_group = H / G;
         p.N = N;
         p.M_dense = T;
-        p.G = split ? 2 : 1;
+        p.G = G;
         p.max_rows = T;
         p.C = logits;
-        p.ldc = split ? 2 * N : N;
+        p.ldc = (long long)G * N;
         p.sC_group = N;
         return launch_gemm(1, GM_F32OUT, p, s);
-    } else if (T < 1024) {
-        // one kernel (one summation order) for every T below the GEMM path, so a token's logits do
-        // not depend on how the tokens are batched
-        dim3 grid((T + 15) / 16, (N + 15) / 16);
-        hipLaunchKernelGGL(k_logits_bf16_sk, grid, dim3(256), 0, s, (const uint16_t*)u, (const uint16_t*)e,
-                           logits, T, H, N);
-    } else if (T >= 2048) {
-        dim3 grid((T + 63) / 64, (N + 63) / 64);
-        hipLaunchKernelGGL(k_logits_bf16<4>, grid, dim3(256), 0, s, (const uint16_t*)u, (const uint16_t*)e,
-                           logits, T, H, N);
-    } else {
-        dim3 grid((T + 15) / 16, (N + 63) / 64);
-        hipLaunchKernelGGL(k_logits_bf16<1>, grid, dim3(256), 0, s, (const uint16_t*)u, (const uint16_t*)e,
-                           logits, T, H, N);
     }
+    dim3 grid((T + 31) / 32, (N + 31) / 32, G);
+    hipLaunchKernelGGL(k_logits_bf16_dec, grid, dim3(64), 0, s, (const uint16_t*)u, (const uint16_t*)e, logits, T, H,
+                       N, G);
     return hipGetLastError();
 }
 
@@ -231,24 +178,15 @@ __device__ __forceinline__ int take_best(unsigned long long (&pk)[NPL], int lane
     return idx;
 }
 
+// Scores, selection and gate weights of token t from its logits l (entry j of a lane: expert
+// lane + 64 j; -inf past N), by one whole wavefront; the results go to a.topk_idx / a.topk_w when
+// `active`.  sh_key: NPL * 64 floats of LDS for this wave (group-limited routing).  Every wave of the
+// workgroup calls this the same number of times (a barrier orders sh_key's writes and reads).
 template <int NPL>
-__global__ __launch_bounds__(256) void k_select(SelectArgs a) {
-    __shared__ float sh_key[4][NPL * 64];
-    const int lane = threadIdx.x & 63;
-    const int wv = threadIdx.x >> 6;
-    const int t_raw = blockIdx.x * 4 + wv;
-    const bool active = t_raw < a.T;
-    const int t = active ? t_raw : a.T - 1;
+__device__ __forceinline__ void select_token(const SelectArgs& a, int t, bool active, float (&l)[NPL],
+                                             float* sh_key, int lane) {
     const int N = a.N;
-
-    float l[NPL], key[NPL], s[NPL];
-#pragma unroll
-    for (int j = 0; j < NPL; ++j) {
-        const int i = lane + 64 * j;
-        l[j] = i >= N ? -INFINITY
-                      : a.split ? a.logits[(size_t)t * 2 * N + i] + a.logits[(size_t)t * 2 * N + N + i]
-                                : a.logits[(size_t)t * N + i];
-    }
+    float key[NPL], s[NPL];
     float lmax = -INFINITY;
 #pragma unroll
     for (int j = 0; j < NPL; ++j) lmax = fmaxf(lmax, l[j]);
@@ -279,12 +217,13 @@ __global__ __launch_bounds__(256) void k_select(SelectArgs a) {
         // group scores: sum of the keys of each contiguous group, in index order
         // (softmax modes: the probabilities s, as ranked; sigmoid mode: s + b)
 #pragma unroll
-        for (int j = 0; j < NPL; ++j) sh_key[wv][lane + 64 * j] = a.gating == 1 ? key[j] : s[j] / z;
+        for (int j = 0; j < NPL; ++j) sh_key[lane + 64 * j] = a.gating == 1 ? key[j] : s[j] / z;
         __syncthreads();
         const int per = N / a.n_group;
         float gs = 0.f;
         if (lane < a.n_group)
-            for (int q = 0; q < per; ++q) gs += sh_key[wv][lane * per + q];
+            for (int q = 0; q < per; ++q) gs += sh_key[lane * per + q];
+        __syncthreads();   // sh_key is rewritten by this wave's next token
         unsigned long long gpk[1] = {lane < a.n_group ? pack_key(gs, lane) : 0ull};
         unsigned long long chosen = 0;
         for (int r = 0; r < a.topk_group; ++r) chosen |= 1ull << take_best<1>(gpk, lane);
@@ -330,6 +269,30 @@ __global__ __launch_bounds__(256) void k_select(SelectArgs a) {
         a.topk_idx[(size_t)t * a.K + lane] = my_idx;
         a.topk_w[(size_t)t * a.K + lane] = g;
     }
+}
+
+// One wavefront per token, logits read from a.logits [T, N].
+template <int NPL>
+__global__ __launch_bounds__(256) void k_select(SelectArgs a) {
+    __shared__ float sh_key[4][NPL * 64];
+    const int lane = threadIdx.x & 63;
+    const int wv = threadIdx.x >> 6;
+    const int t_raw = blockIdx.x * 4 + wv;
+    const bool active = t_raw < a.T;
+    const int t = active ? t_raw : a.T - 1;
+    float l[NPL];
+    const float* row = a.logits + (size_t)t * a.groups * a.N;
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) {
+        const int i = lane + 64 * j;
+        float v = -INFINITY;
+        if (i < a.N) {
+            v = row[i];
+            for (int g = 1; g < a.groups; ++g) v += row[(size_t)g * a.N + i];
+        }
+        l[j] = v;
+    }
+    select_token<NPL>(a, t, active, l, sh_key[wv], lane);
 }
 
 hipError_t launch_select(const SelectArgs& a, hipStream_t s) {

@@ -36,9 +36,17 @@ def test_c4_prefill_skewed_loads(c4):
     say("[c4] near ties %d, empty %d, max/mean %.1f, max/min nonzero %.1f" % (
         stats["near_ties"], (c == 0).sum(), c.max() / c.mean(), nz.max() / nz.min()))
     assert c.max() / c.mean() > 20.0   # loads span more than 20x: overfull and empty groups
+    PREFILL["idx"], PREFILL["wts"] = idx[:64].clone(), wts[:64].clone()
+
+
+PREFILL = {}
 
 
 def test_c4_decode(c4):
     case = c4.with_tokens(64)
     case.w = case.w.with_(name="c4d")
-    layer_parity(case, route_all=True, label="c4d")
+    _, (out, idx, wts) = layer_parity(case, route_all=True, label="c4d")
+    if PREFILL:   # the same routing as in the prefill batch, bit for bit (one canonical logit order)
+        import torch
+        assert torch.equal(idx, PREFILL["idx"])
+        assert torch.equal(wts.view(torch.int32), PREFILL["wts"].view(torch.int32))

@@ -35,6 +35,9 @@ def load_stats(idx, N):
     return dict(touched=int((c > 0).sum()), empty=int((c == 0).sum()), max_over_mean=float(c.max() / c.mean()))
 
 
+PREFILL = {}
+
+
 def test_v3_prefill(v3):
     w = v3.w
     stats, (out, idx, wts) = layer_parity(v3, tokens=strided_tokens(w.T, 8), route_all=True, label="c3p",
@@ -44,6 +47,7 @@ def test_v3_prefill(v3):
         stats["near_ties"], ls, stats["tokens_checked"], stats["routed_m_tiles"], stats["tokens_added_for_tiles"]))
     assert ls["empty"] < w.N_r
     assert stats["tokens_checked"] >= w.T // 8
+    PREFILL["idx"], PREFILL["wts"] = idx[:128].clone(), wts[:128].clone()
 
 
 def test_v3_decode(v3):
@@ -51,3 +55,9 @@ def test_v3_decode(v3):
     case.w = case.w.with_(name="c3d")
     stats, (out, idx, wts) = layer_parity(case, route_all=True, label="c3d")
     say("[v3] decode near ties %d, load %s" % (stats["near_ties"], load_stats(idx, case.w.N_r)))
+    if PREFILL:
+        # one canonical order for the logits: the decode step routes its tokens exactly as the prefill
+        # batch did (different kernels), near ties included
+        import torch
+        assert torch.equal(idx, PREFILL["idx"])
+        assert torch.equal(wts.view(torch.int32), PREFILL["wts"].view(torch.int32))
