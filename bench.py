@@ -207,7 +207,7 @@ def _simd_count(d, default=1024):
     return default
 
 
-def counter_summary(pmc_dir, fetch_dir=None, write_dir=None, copy_bytes=COPY_BYTES):
+def counter_summary(pmc_dir, fetch_dir=None, write_dir=None, copy_bytes=COPY_BYTES, rdreq_dir=None):
     """Per-kernel table of a rocprofv3 run with --pmc SQ_VALU_MFMA_BUSY_CYCLES MfmaUtil GRBM_GUI_ACTIVE
     SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_BUSY_CYCLES --kernel-trace, plus optional FETCH_SIZE and WRITE_SIZE runs.
 
@@ -248,9 +248,19 @@ def counter_summary(pmc_dir, fetch_dir=None, write_dir=None, copy_bytes=COPY_BYT
                 if f and w:
                     traffic[_short(k)] = (sum(f) / len(f) * 1024 * sf, sum(w) / len(w) * 1024 * sw)
             traffic["_scales"] = (sf, sw, copy_f, copy_w)
+    rdreq = {}
+    if rdreq_dir:
+        # bytes of the L2-to-fabric read requests by size: 128 x RDREQ_128B + 64 x RDREQ_64B + 32 x RDREQ_32B
+        rc = _read_counters(rdreq_dir)
+        for k, d in rc.items():
+            n = len(d.get("TCC_EA0_RDREQ_128B_sum", []))
+            if n:
+                b = (128 * sum(d["TCC_EA0_RDREQ_128B_sum"]) + 64 * sum(d.get("TCC_EA0_RDREQ_64B_sum", [0])) +
+                     32 * sum(d.get("TCC_EA0_RDREQ_32B_sum", [0])))
+                rdreq[_short(k)] = b / n
     lines = ["| kernel | dispatches | avg ms | MFMA busy % | shader clock GHz | executed bf16 TFLOP/s |"
-             " read GB | written GB | HBM TB/s |",
-             "|---|---|---|---|---|---|---|---|---|"]
+             " read GB | written GB | HBM TB/s |" + (" read GB (requests) |" if rdreq else ""),
+             "|---|---|---|---|---|---|---|---|---|" + ("---|" if rdreq else "")]
     res = {}
     for k in sorted(per, key=lambda k: -per[k]["ns"]):
         a = per[k]
@@ -269,7 +279,8 @@ def counter_summary(pmc_dir, fetch_dir=None, write_dir=None, copy_bytes=COPY_BYT
                   "executed_tflops": tfs, "read_bytes": rd, "write_bytes": wr}
         lines.append("| %s | %d | %.4f | %.1f | %s | %.0f | %s | %s | %s |" % (
             k, n, ms, util, "-" if clk != clk else "%.2f" % clk, tfs, "-" if rd is None else "%.3f" % (rd / 1e9),
-            "-" if wr is None else "%.3f" % (wr / 1e9), "-" if tbs is None else "%.2f" % tbs))
+            "-" if wr is None else "%.3f" % (wr / 1e9), "-" if tbs is None else "%.2f" % tbs) +
+            ((" %s |" % ("-" if k not in rdreq else "%.3f" % (rdreq[k] / 1e9))) if rdreq else ""))
     if "_scales" in traffic:
         sf, sw, cf, cw = traffic["_scales"]
         lines.append("")
@@ -510,13 +521,14 @@ def main():
     ap.add_argument("--traffic-json", metavar="FILE")
     ap.add_argument("--counter-summary", metavar="PMC_DIR",
                     help="per-kernel MFMA busy %%, shader clock and HBM bytes of rocprofv3 --pmc runs, then exit")
+    ap.add_argument("--pmc-rdreq", metavar="DIR", help="a TCC_EA0_RDREQ*_sum run for --counter-summary")
     ap.add_argument("--weights", choices=("packed", "unpacked"), default="packed",
                     help="routed expert banks in fragment order (moe_pack_weights, done once when the weights "
                          "are loaded, before timing; the layer's output is bit-identical) or in the [out, in] "
                          "layout")
     args = ap.parse_args()
     if args.counter_summary:
-        text, _ = counter_summary(args.counter_summary, args.pmc_fetch, args.pmc_write)
+        text, _ = counter_summary(args.counter_summary, args.pmc_fetch, args.pmc_write, rdreq_dir=args.pmc_rdreq)
         print(text)
         return
     if args.rocprof_summary:
