@@ -289,6 +289,48 @@ def counter_summary(pmc_dir, fetch_dir=None, write_dir=None, copy_bytes=COPY_BYT
     return "\n".join(lines), res
 
 
+def power_summary(log, busy_mhz=1000.0):
+    """Socket power and shader clocks from a log of `amd-smi metric --power --clock --json` samples, each
+    preceded by a line `t=<unix seconds> phase=<label>` (the label names what the GPU was running):
+    medians per phase over the samples with the clocks above busy_mhz (the GPU working)."""
+    import re
+    import statistics
+    with open(log) as fh:
+        txt = fh.read()
+    parts = re.split(r"^t=([\d.]+)(?: phase=(\S+))?\n", txt, flags=re.M)
+    rows = []
+    for i in range(1, len(parts), 3):
+        body = parts[i + 2]
+        if "{" not in body:
+            continue
+        try:
+            g = json.loads(body[body.index("{"):])["gpu_data"][0]
+        except (ValueError, KeyError, IndexError):
+            continue
+        clk = [v["clk"]["value"] for k, v in g.get("clock", {}).items()
+               if k.startswith("gfx_") and isinstance(v.get("clk", {}).get("value"), (int, float))]
+        pw = g.get("power", {}).get("socket_power", {}).get("value")
+        if clk and isinstance(pw, (int, float)):
+            rows.append((float(parts[i]), parts[i + 1] or "-", float(pw), sum(clk) / len(clk)))
+    lines = ["| phase | busy samples | socket power W (median / max) | mean shader clock MHz (median) |",
+             "|---|---|---|---|"]
+    phases = []
+    for r in rows:
+        if r[1] not in phases:
+            phases.append(r[1])
+    for ph in phases:
+        sel = [r for r in rows if r[1] == ph and r[3] > busy_mhz]
+        if sel:
+            lines.append("| %s | %d | %.0f / %.0f | %.0f |" % (ph, len(sel), statistics.median(r[2] for r in sel),
+                                                              max(r[2] for r in sel), statistics.median(r[3] for r in sel)))
+    idle = [r for r in rows if r[3] <= busy_mhz]
+    if idle:
+        lines.append("")
+        lines.append("%d samples with the GPU idle (clocks below %.0f MHz): socket power median %.0f W." % (
+            len(idle), busy_mhz, statistics.median(r[2] for r in idle)))
+    return "\n".join(lines), rows
+
+
 # ---------------------------------------------------------------- timing helpers
 
 def _upload(inp):
@@ -522,6 +564,8 @@ def main():
     ap.add_argument("--counter-summary", metavar="PMC_DIR",
                     help="per-kernel MFMA busy %%, shader clock and HBM bytes of rocprofv3 --pmc runs, then exit")
     ap.add_argument("--pmc-rdreq", metavar="DIR", help="a TCC_EA0_RDREQ*_sum run for --counter-summary")
+    ap.add_argument("--power-summary", metavar="LOG",
+                    help="socket power and shader clocks from a log of amd-smi metric samples, then exit")
     ap.add_argument("--weights", choices=("packed", "unpacked"), default="packed",
                     help="routed expert banks in fragment order (moe_pack_weights, done once when the weights "
                          "are loaded, before timing; the layer's output is bit-identical) or in the [out, in] "
@@ -530,6 +574,9 @@ def main():
     if args.counter_summary:
         text, _ = counter_summary(args.counter_summary, args.pmc_fetch, args.pmc_write, rdreq_dir=args.pmc_rdreq)
         print(text)
+        return
+    if args.power_summary:
+        print(power_summary(args.power_summary)[0])
         return
     if args.rocprof_summary:
         text, _ = rocprof_summary(args.rocprof_summary, args.pmc_fetch, args.pmc_write, args.traffic_json,
@@ -639,6 +686,7 @@ def main():
 
     if not args.no_decode:
         Td = args.decode_tokens
+        print("[bench] timing decode, T=%d" % Td, file=sys.stderr, flush=True)
         wd = w.with_(T=Td)
         sd = moe.make_shape(Td, w.H, w.N_r, w.K_r, w.Ks, w.I, w.gating, w.act, w.dtype)
         wsd = moe.workspace(sd)
@@ -666,6 +714,7 @@ def main():
         print("[bench] decode %.3f ms/step, %.0f GB/s" % (dms, gbs), file=sys.stderr, flush=True)
         if w.gating == 1:
             # sensitivity: the selection bias set to 0 (near-uniform routing touches almost every expert)
+            print("[bench] timing decode with the selection bias set to 0", file=sys.stderr, flush=True)
             zfn, zidx = _layer_call(w, d, flags, T=Td, bias=None)
             zms = _time_steps(zfn, max(args.steps, 10), args.warmup)
             zt = int(np.unique(zidx.cpu().numpy()).size)

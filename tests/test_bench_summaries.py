@@ -1,6 +1,7 @@
-"""The bench's rocprofv3 summaries (host logic, CPU only): per-kernel counter arithmetic, the HBM byte
-scaling from the device copy, and the gate that keeps stale traffic figures out of the bench line.
-The CSV files are small synthetic stand-ins with the columns rocprofv3 writes."""
+"""The bench's profiling summaries (host logic, CPU only): per-kernel counter arithmetic, the HBM byte
+scaling from the device copy, the gate that keeps stale traffic figures out of the bench line, and the
+per-phase power and clock table.  The CSV files are small synthetic stand-ins with the columns rocprofv3
+writes; the power log imitates `amd-smi metric --power --clock --json` output."""
 import csv
 import json
 import math
@@ -118,3 +119,19 @@ def test_committed_traffic_figure_matches_the_sources():
     assert t["traffic_bytes_per_launch"] > 0
     assert t["fetch_scale"] == pytest.approx(2.0, rel=1e-3)
     assert t["write_scale"] == pytest.approx(1.0, rel=1e-3)
+
+
+def test_power_summary_per_phase(tmp_path):
+    def sample(t, phase, watts, clocks):
+        g = {"gpu": 0, "power": {"socket_power": {"value": watts, "unit": "W"}},
+             "clock": {"gfx_%d" % i: {"clk": {"value": c, "unit": "MHz"}} for i, c in enumerate(clocks)}}
+        return "t=%.3f phase=%s\n%s\n" % (t, phase, json.dumps({"gpu_data": [g]}, indent=1))
+    log = tmp_path / "samples.log"
+    log.write_text(sample(0.0, "setup", 250, [100] * 8) + sample(0.1, "prefill", 1398, [1600] * 8) +
+                   sample(0.2, "prefill", 1402, [1580, 1620] * 4) + sample(0.3, "prefill", 1400, [1600] * 8) +
+                   sample(0.4, "decode", 1270, [2380] * 8) + "t=0.5 phase=decode\nnot json\n")
+    text, rows = bench.power_summary(str(log))
+    assert len(rows) == 5
+    assert "| prefill | 3 | 1400 / 1402 | 1600 |" in text
+    assert "| decode | 1 | 1270 / 1270 | 2380 |" in text
+    assert "1 samples with the GPU idle" in text and "median 250 W" in text
